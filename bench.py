@@ -1,0 +1,175 @@
+"""Benchmark: one context-parallel rank's ring-attention forward on one MI355X.
+
+A step is one whole pass of the path: cp_attn_rank_forward for the last rank
+of the 128K-token example split over 4 ranks (S=131072, N=4, L=32768, rank 3,
+causal, B=1, H=32, d=128, bf16): ring schedule, simulated ring receives of
+blocks 2, 1, 0 into the two workspace slots on a second stream (double
+buffered), four attention kernels (diagonal block first) and the fused
+finalise.  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line.  The metric is causal-adjusted attention TFLOP/s:
+4 d B H x (visible query/key pairs) flops per step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk (the published 2.5 PF)
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="query rows of one head timed on the CPU oracle")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(spec, q, k, v, rows_n: int):
+    """The fp64 oracle, as it is, on a bounded sample of the same workload:
+    `rows_n` evenly spaced query rows of head 0, against all keys."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = 1
+    L = spec.L
+    rows = np.linspace(0, L - 1, rows_n).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.rank_attention(q, k, v, spec.rank, spec.N, spec.mask, spec.cu_seqlens, rows=rows, heads=[0])
+    dt = time.perf_counter() - t0
+    p = spec.rank * L + rows
+    pairs = int(np.sum(p + 1)) if spec.mask == "causal" else int(rows_n * spec.S)
+    flops = 4.0 * spec.d * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{rows_n} evenly spaced query rows of head 0 of 32 ({pairs} visible pairs, "
+                      f"{dt:.1f} s wall, fp64 numpy, materialised score rows)",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import context_ring_attention_cp_amd as cp
+    from harness.inputs import TENSOR_K, TENSOR_Q, TENSOR_V, bf16_bits, draw_shard, standard_configs
+
+    cp.lib()
+    spec = standard_configs(args.seed)[3]
+    N, L, H, d, r = spec.N, spec.L, spec.H, spec.d, spec.rank
+    log(f"[bench] generating inputs for {spec.name}")
+    q = draw_shard(spec, args.seed, TENSOR_Q, r)
+    k = {j: draw_shard(spec, args.seed, TENSOR_K, j) for j in range(N)}
+    v = {j: draw_shard(spec, args.seed, TENSOR_V, j) for j in range(N)}
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(bf16_bits(x)).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+    qd = dev(q)
+    kd = [dev(k[j]) for j in range(N)]
+    vd = [dev(v[j]) for j in range(N)]
+    desc = cp.Desc(spec.B, H, d, N, L, r, "bf16", "causal")
+    out = torch.empty((spec.B, L, H, d), dtype=torch.bfloat16, device="cuda")
+    m = torch.empty((spec.B, H, L), device="cuda")
+    lsum = torch.empty_like(m)
+    lse = torch.empty_like(m)
+    ws = cp.alloc_workspace(desc)
+    cs, xs = torch.cuda.Stream(), torch.cuda.Stream()
+    sched = cp.cp_attn_ring_schedule(desc, cp.CP_RING_PREFETCH)
+    prof = cp.Profiler(len(sched) * max(args.steps, 1))
+    pairs = cp.cp_attn_visible_pairs(desc)
+    flops = 4.0 * d * spec.B * H * pairs
+    torch.cuda.synchronize()
+
+    def step(p=None):
+        cp.cp_attn_rank_forward(desc, qd, kd, vd, out, m, lsum, lse, workspace=ws, compute_stream=cs,
+                                copy_stream=xs, flags=cp.CP_RING_PREFETCH, profiler=p)
+
+    log(f"[bench] warmup {args.warmup} steps, schedule {sched}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    prof.reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(cs)
+    for _ in range(args.steps):
+        step(prof)
+    e1.record(cs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    kernel_ms = prof.read()
+    assert torch.isfinite(out.float()).all(), "non-finite output"
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    # dominant kernel: the attention block kernel; achieved = algorithmic flops
+    # of its launches / their summed duration (= mean flops per launch / mean duration)
+    k_sum = sum(kernel_ms)
+    achieved = flops * args.steps / (k_sum * 1e-3) / 1e12
+    per_step = [kernel_ms[i:i + len(sched)] for i in range(0, len(kernel_ms), len(sched))]
+    blk_bytes = spec.B * L * H * d * 2
+    res = {
+        "metric": "causal-adjusted attention TFLOP/s per rank shard; % of MI355X bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal last-rank shard of the 128K example: S=131072 N=4 L=32768 rank=3 "
+                               "B=1 H=32 d=128 bf16, simulated ring with double-buffered prefetch",
+                   "S": spec.S, "N": N, "L": L, "rank": r, "B": spec.B, "H": H, "d": d, "mask": "causal",
+                   "seed": args.seed},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "flops_per_step": flops,
+        "kernel_ms_per_step": [round(x, 4) for x in per_step[-1]] if per_step else [],
+        "kernel_mean_ms": round(k_sum / max(1, len(kernel_ms)), 4),
+        "ring_bytes_copied_per_step": 2 * blk_bytes * (len(sched) - 1),
+        "ring_traffic_formula_bytes": 2 * (2 * spec.B * spec.S * H * d * 2 // N) * (N - 1),
+        "wall_s_timed": round(wall, 3),
+    }
+    prof.close()
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows of head 0")
+        res["cpu_baseline"] = cpu_baseline(spec, q, k, v, args.cpu_rows)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,513 @@
+// Host side of libcpattn: argument validation, the ring schedule with
+// mask-aware block skipping, workspace layout, and the one-GPU ring driver
+// (two receive slots, a copy stream, events).  Every public entry point
+// validates all of its arguments before it makes any HIP call, so invalid
+// calls fail without touching a device.
+#include "../../include/cpattn.h"
+#include "kernels.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+using namespace cpattn;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+cp_status fail(cp_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+cp_status hip_fail(hipError_t e, const char* what) {
+  return fail(CP_ERR_HIP, "%s failed: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elt_bytes(int32_t dtype) { return dtype == CP_BF16 ? 2 : 4; }
+
+// Validation of the description alone (no pointers of tensors).
+cp_status check_desc(const cp_attn_desc* d) {
+  if (!d) return fail(CP_ERR_INVALID_ARG, "desc is NULL");
+  if (d->B < 1 || d->H < 1) return fail(CP_ERR_INVALID_ARG, "B=%d and H=%d must be >= 1", d->B, d->H);
+  if (d->L < 1) return fail(CP_ERR_INVALID_ARG, "L=%lld must be >= 1", (long long)d->L);
+  if (d->N < 1 || d->N > CP_MAX_RING)
+    return fail(CP_ERR_INVALID_ARG, "ring size N=%d outside [1, %d]", d->N, CP_MAX_RING);
+  if (d->rank < 0 || d->rank >= d->N)
+    return fail(CP_ERR_INVALID_ARG, "rank=%d outside [0, N=%d)", d->rank, d->N);
+  if (d->dtype != CP_F32 && d->dtype != CP_BF16) return fail(CP_ERR_INVALID_ARG, "dtype=%d unknown", d->dtype);
+  if (d->mask != CP_MASK_NONE && d->mask != CP_MASK_CAUSAL && d->mask != CP_MASK_DOC_CAUSAL)
+    return fail(CP_ERR_INVALID_ARG, "mask=%d unknown", d->mask);
+  if (!(std::isfinite(d->scale) && d->scale >= 0.f))
+    return fail(CP_ERR_INVALID_ARG, "scale=%g must be finite and >= 0", (double)d->scale);
+  if (d->d != 64 && d->d != 128) return fail(CP_ERR_UNSUPPORTED, "head dim d=%d not in {64, 128}", d->d);
+  // sizes: total sequence and element counts must stay well inside int64 and
+  // the sequence positions inside int32 (cu_seqlens are int32)
+  const long double S = (long double)d->N * (long double)d->L;
+  if (S > 2147483647.0L) return fail(CP_ERR_UNSUPPORTED, "sequence N*L=%.0Lf exceeds int32 positions", S);
+  const long double elems = (long double)d->B * d->L * d->H * d->d;
+  if (elems * 4 > 4.0e18L) return fail(CP_ERR_UNSUPPORTED, "tensor of %.0Lf elements too large", elems);
+  // launch grid of the widest kernel (one workgroup per 64 rows of a head)
+  const long double wgs = (long double)d->B * d->H * ((d->L + 63) / 64);
+  if (wgs > 2147483647.0L) return fail(CP_ERR_UNSUPPORTED, "launch grid of %.0Lf workgroups too large", wgs);
+  const long double thr = elems / 4;
+  if (thr / 256 > 2147483647.0L) return fail(CP_ERR_UNSUPPORTED, "elementwise grid too large");
+  if (d->mask == CP_MASK_DOC_CAUSAL) {
+    if (!d->cu_seqlens || !d->cu_seqlens_dev)
+      return fail(CP_ERR_INVALID_ARG, "DOC_CAUSAL needs cu_seqlens (host) and cu_seqlens_dev (device)");
+    if (d->ndocs < 1) return fail(CP_ERR_INVALID_ARG, "ndocs=%d must be >= 1", d->ndocs);
+    if (!aligned(d->cu_seqlens_dev, 4)) return fail(CP_ERR_INVALID_ARG, "cu_seqlens_dev not 4-byte aligned");
+    const int32_t* cu = d->cu_seqlens;
+    if (cu[0] != 0) return fail(CP_ERR_INVALID_ARG, "cu_seqlens[0]=%d must be 0", cu[0]);
+    for (int32_t k = 0; k < d->ndocs; ++k)
+      if (cu[k + 1] <= cu[k])
+        return fail(CP_ERR_INVALID_ARG, "cu_seqlens not strictly increasing at %d (%d, %d)", k, cu[k], cu[k + 1]);
+    if ((int64_t)cu[d->ndocs] != (int64_t)d->N * d->L)
+      return fail(CP_ERR_INVALID_ARG, "cu_seqlens[ndocs]=%d must equal N*L=%lld", cu[d->ndocs],
+                  (long long)d->N * d->L);
+  }
+  return CP_OK;
+}
+
+cp_status check_tensor(const void* p, const char* name) {
+  if (!p) return fail(CP_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(p, 16)) return fail(CP_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return CP_OK;
+}
+
+cp_status check_vec(const void* p, const char* name, bool optional) {
+  if (!p) return optional ? CP_OK : fail(CP_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(p, 4)) return fail(CP_ERR_INVALID_ARG, "%s is not 4-byte aligned", name);
+  return CP_OK;
+}
+
+// First position of the document holding global position p (host cu).
+int64_t doc_start_host(const cp_attn_desc* d, int64_t p) {
+  int lo = 0, hi = d->ndocs;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if ((int64_t)d->cu_seqlens[mid] <= p) lo = mid; else hi = mid;
+  }
+  return d->cu_seqlens[lo];
+}
+
+// Does any row of the rank see any key of block j?  Causal forms: row p sees
+// keys up to p, so block j > rank is invisible and block rank always visible;
+// for an earlier block the rows with the earliest first key is the shard's
+// first row (doc_start is non-decreasing in p).
+bool block_visible(const cp_attn_desc* d, int32_t j) {
+  if (d->mask == CP_MASK_NONE) return true;
+  if (j > d->rank) return false;
+  if (j == d->rank || d->mask == CP_MASK_CAUSAL) return true;
+  const int64_t first = doc_start_host(d, (int64_t)d->rank * d->L);
+  return first <= (int64_t)(j + 1) * d->L - 1;
+}
+
+std::vector<int32_t> schedule(const cp_attn_desc* d, int32_t flags) {
+  std::vector<int32_t> out;
+  const int step = (flags & CP_RING_REVERSE) ? 1 : -1;
+  for (int32_t t = 0; t < d->N; ++t) {
+    const int32_t j = (int32_t)((((int64_t)d->rank + step * t) % d->N + d->N) % d->N);
+    if (block_visible(d, j)) out.push_back(j);
+  }
+  return out;
+}
+
+float scale_log2(const cp_attn_desc* d) {
+  const float sc = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)d->d);
+  return sc * 1.442695040888963407360f;
+}
+
+BlockArgs block_args(const cp_attn_desc* d, int32_t j, const void* q, const void* k, const void* v) {
+  BlockArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.L = d->L;
+  a.B = d->B;
+  a.H = d->H;
+  a.q_pos0 = (int64_t)d->rank * d->L;
+  a.k_pos0 = (int64_t)j * d->L;
+  a.mask = d->mask;
+  a.ndocs = d->ndocs;
+  a.cu = d->mask == CP_MASK_DOC_CAUSAL ? d->cu_seqlens_dev : nullptr;
+  a.scale_log2 = scale_log2(d);
+  return a;
+}
+
+hipError_t launch_block(const cp_attn_desc* d, const BlockArgs& a, hipStream_t s) {
+  return d->dtype == CP_BF16 ? launch_block_bf16(a, d->d, s) : launch_block_f32(a, d->d, s);
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct WorkspaceLayout {
+  size_t slot_k[2], slot_v[2], st_o, st_m, st_l, total;
+};
+
+WorkspaceLayout layout_of(const cp_attn_desc* d) {
+  WorkspaceLayout w;
+  const size_t blk = round_up((size_t)d->B * d->L * d->H * d->d * elt_bytes(d->dtype), 256);
+  const size_t ost = round_up((size_t)d->B * d->L * d->H * d->d * 4, 256);
+  const size_t vec = round_up((size_t)d->B * d->H * d->L * 4, 256);
+  size_t off = 0;
+  for (int s = 0; s < 2; ++s) {
+    w.slot_k[s] = off;
+    off += blk;
+    w.slot_v[s] = off;
+    off += blk;
+  }
+  w.st_o = off;
+  off += ost;
+  w.st_m = off;
+  off += vec;
+  w.st_l = off;
+  off += vec;
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+struct cp_attn_profiler {
+  std::vector<hipEvent_t> start, stop;
+  int32_t used = 0;
+};
+
+extern "C" {
+
+const char* cp_attn_status_string(int32_t status) {
+  switch (status) {
+    case CP_OK: return "CP_OK";
+    case CP_ERR_INVALID_ARG: return "CP_ERR_INVALID_ARG";
+    case CP_ERR_UNSUPPORTED: return "CP_ERR_UNSUPPORTED";
+    case CP_ERR_WORKSPACE: return "CP_ERR_WORKSPACE";
+    case CP_ERR_HIP: return "CP_ERR_HIP";
+    default: return "CP_ERR_UNKNOWN";
+  }
+}
+
+const char* cp_attn_last_error(void) { return g_last_error.c_str(); }
+
+cp_status cp_attn_ring_schedule(const cp_attn_desc* desc, int32_t flags, int32_t* blocks_out,
+                                int32_t capacity, int32_t* count_out) {
+  g_last_error.clear();
+  cp_status st = check_desc(desc);
+  if (st != CP_OK) return st;
+  if (!count_out) return fail(CP_ERR_INVALID_ARG, "count_out is NULL");
+  if (flags & ~(CP_RING_PREFETCH | CP_RING_REVERSE)) return fail(CP_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  const std::vector<int32_t> s = schedule(desc, flags);
+  if (capacity < (int32_t)s.size() || (!blocks_out && !s.empty()))
+    return fail(CP_ERR_INVALID_ARG, "capacity %d < %zu scheduled blocks", capacity, s.size());
+  for (size_t i = 0; i < s.size(); ++i) blocks_out[i] = s[i];
+  *count_out = (int32_t)s.size();
+  return CP_OK;
+}
+
+cp_status cp_attn_visible_pairs(const cp_attn_desc* desc, int64_t* pairs_out) {
+  g_last_error.clear();
+  cp_status st = check_desc(desc);
+  if (st != CP_OK) return st;
+  if (!pairs_out) return fail(CP_ERR_INVALID_ARG, "pairs_out is NULL");
+  const int64_t L = desc->L, r = desc->rank;
+  const int64_t s0 = r * L, s1 = (r + 1) * L;     // rows [s0, s1)
+  int64_t pairs = 0;
+  if (desc->mask == CP_MASK_NONE) {
+    pairs = (int64_t)desc->N * L * L;
+  } else if (desc->mask == CP_MASK_CAUSAL) {
+    pairs = s0 * L + L * (L + 1) / 2;             // sum over p of (p + 1)
+  } else {
+    // sum over rows p of (p - doc_start(p) + 1), one document at a time
+    for (int32_t k = 0; k < desc->ndocs; ++k) {
+      const int64_t a = desc->cu_seqlens[k], e = desc->cu_seqlens[k + 1];
+      const int64_t lo = a > s0 ? a : s0, hi = e < s1 ? e : s1;   // rows [lo, hi)
+      if (lo >= hi) continue;
+      const int64_t n = hi - lo, first = lo - a + 1;              // first + (first+1) + ... n terms
+      pairs += n * first + n * (n - 1) / 2;
+    }
+  }
+  *pairs_out = pairs;
+  return CP_OK;
+}
+
+size_t cp_attn_workspace_bytes(const cp_attn_desc* desc) {
+  g_last_error.clear();
+  if (check_desc(desc) != CP_OK) return 0;
+  return layout_of(desc).total;
+}
+
+cp_status cp_attn_block_partial(const cp_attn_desc* desc, int32_t j, int32_t mode, const void* q,
+                                const void* k_j, const void* v_j, const cp_state* state, float* o_part,
+                                float* lse_part, void* stream) {
+  g_last_error.clear();
+  cp_status st = check_desc(desc);
+  if (st != CP_OK) return st;
+  if (j < 0 || j >= desc->N) return fail(CP_ERR_INVALID_ARG, "block j=%d outside [0, N=%d)", j, desc->N);
+  if ((st = check_tensor(q, "q")) != CP_OK || (st = check_tensor(k_j, "k_j")) != CP_OK ||
+      (st = check_tensor(v_j, "v_j")) != CP_OK)
+    return st;
+  BlockArgs a = block_args(desc, j, q, k_j, v_j);
+  if (mode == CP_MODE_INIT || mode == CP_MODE_ACCUMULATE) {
+    if (!state) return fail(CP_ERR_INVALID_ARG, "state is NULL for mode %d", mode);
+    if (o_part || lse_part) return fail(CP_ERR_INVALID_ARG, "o_part/lse_part must be NULL for mode %d", mode);
+    if ((st = check_tensor(state->o, "state->o")) != CP_OK || (st = check_vec(state->m, "state->m", false)) != CP_OK ||
+        (st = check_vec(state->l, "state->l", false)) != CP_OK)
+      return st;
+    a.st_o = state->o;
+    a.st_m = state->m;
+    a.st_l = state->l;
+    a.flags = F_WRITE_STATE | (mode == CP_MODE_ACCUMULATE ? F_READ_STATE : 0);
+  } else if (mode == CP_MODE_PARTIAL_LSE) {
+    if (state) return fail(CP_ERR_INVALID_ARG, "state must be NULL for PARTIAL_LSE");
+    if ((st = check_tensor(o_part, "o_part")) != CP_OK || (st = check_vec(lse_part, "lse_part", false)) != CP_OK)
+      return st;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    a.flags = F_WRITE_PARTIAL;
+  } else {
+    return fail(CP_ERR_INVALID_ARG, "mode=%d unknown", mode);
+  }
+  const hipError_t e = launch_block(desc, a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "block kernel launch");
+  return CP_OK;
+}
+
+cp_status cp_attn_merge_lse(const cp_attn_desc* desc, int32_t n, const float* const* o_parts,
+                            const float* const* lse_parts, const int32_t* order, void* out, float* lse_out,
+                            void* stream) {
+  g_last_error.clear();
+  cp_status st = check_desc(desc);
+  if (st != CP_OK) return st;
+  if (n < 1 || n > CP_MAX_RING || n > kMaxParts) return fail(CP_ERR_INVALID_ARG, "n=%d outside [1, %d]", n, CP_MAX_RING);
+  if (!o_parts || !lse_parts) return fail(CP_ERR_INVALID_ARG, "o_parts/lse_parts is NULL");
+  if ((st = check_tensor(out, "out")) != CP_OK || (st = check_vec(lse_out, "lse_out", true)) != CP_OK) return st;
+  MergeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  std::vector<char> seen(n, 0);
+  for (int32_t t = 0; t < n; ++t) {
+    const int32_t j = order ? order[t] : t;
+    if (j < 0 || j >= n || seen[j]) return fail(CP_ERR_INVALID_ARG, "order is not a permutation of 0..%d", n - 1);
+    seen[j] = 1;
+    if ((st = check_tensor(o_parts[j], "o_parts[j]")) != CP_OK || (st = check_vec(lse_parts[j], "lse_parts[j]", false)) != CP_OK)
+      return st;
+    a.o[t] = o_parts[j];
+    a.lse[t] = lse_parts[j];
+  }
+  a.n = n;
+  a.L = desc->L;
+  a.B = desc->B;
+  a.H = desc->H;
+  a.d = desc->d;
+  a.out_bf16 = desc->dtype == CP_BF16;
+  a.out = out;
+  a.lse_out = lse_out;
+  const hipError_t e = launch_merge(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  return CP_OK;
+}
+
+cp_status cp_attn_finalize(const cp_attn_desc* desc, const cp_state* state, void* out, float* m_out,
+                           float* l_out, float* lse_out, void* stream) {
+  g_last_error.clear();
+  cp_status st = check_desc(desc);
+  if (st != CP_OK) return st;
+  if (!state) return fail(CP_ERR_INVALID_ARG, "state is NULL");
+  if ((st = check_tensor(state->o, "state->o")) != CP_OK || (st = check_vec(state->m, "state->m", false)) != CP_OK ||
+      (st = check_vec(state->l, "state->l", false)) != CP_OK || (st = check_tensor(out, "out")) != CP_OK ||
+      (st = check_vec(m_out, "m_out", true)) != CP_OK || (st = check_vec(l_out, "l_out", true)) != CP_OK ||
+      (st = check_vec(lse_out, "lse_out", true)) != CP_OK)
+    return st;
+  FinalizeArgs a;
+  a.st_o = state->o;
+  a.st_m = state->m;
+  a.st_l = state->l;
+  a.L = desc->L;
+  a.B = desc->B;
+  a.H = desc->H;
+  a.d = desc->d;
+  a.out_bf16 = desc->dtype == CP_BF16;
+  a.out = out;
+  a.m_out = m_out;
+  a.l_out = l_out;
+  a.lse_out = lse_out;
+  const hipError_t e = launch_finalize(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "finalize kernel launch");
+  return CP_OK;
+}
+
+cp_status cp_attn_rank_forward(const cp_attn_desc* desc, const void* q, const void* const* k_blocks,
+                               const void* const* v_blocks, void* out, float* m_out, float* l_out, float* lse_out,
+                               void* workspace, size_t workspace_bytes, void* compute_stream, void* copy_stream,
+                               int32_t flags, cp_attn_profiler* prof) {
+  g_last_error.clear();
+  cp_status st = check_desc(desc);
+  if (st != CP_OK) return st;
+  if (flags & ~(CP_RING_PREFETCH | CP_RING_REVERSE)) return fail(CP_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if ((st = check_tensor(q, "q")) != CP_OK || (st = check_tensor(out, "out")) != CP_OK ||
+      (st = check_vec(m_out, "m_out", true)) != CP_OK || (st = check_vec(l_out, "l_out", true)) != CP_OK ||
+      (st = check_vec(lse_out, "lse_out", true)) != CP_OK)
+    return st;
+  if (!k_blocks || !v_blocks) return fail(CP_ERR_INVALID_ARG, "k_blocks/v_blocks is NULL");
+  const std::vector<int32_t> sched = schedule(desc, flags);
+  for (int32_t j : sched) {
+    if ((st = check_tensor(k_blocks[j], "k_blocks[j]")) != CP_OK || (st = check_tensor(v_blocks[j], "v_blocks[j]")) != CP_OK)
+      return st;
+  }
+  const WorkspaceLayout wl = layout_of(desc);
+  if (!workspace) return fail(CP_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(CP_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < wl.total)
+    return fail(CP_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, wl.total);
+  const bool prefetch = flags & CP_RING_PREFETCH;
+  if (prefetch && (copy_stream == compute_stream))
+    return fail(CP_ERR_INVALID_ARG, "CP_RING_PREFETCH needs a copy_stream distinct from compute_stream");
+  if (sched.empty()) return fail(CP_ERR_INVALID_ARG, "no visible block");   // unreachable: the diagonal is visible
+
+  hipStream_t cs = (hipStream_t)compute_stream;
+  hipStream_t xs = (hipStream_t)copy_stream;
+  char* ws = (char*)workspace;
+  const size_t blk_bytes = (size_t)desc->B * desc->L * desc->H * desc->d * elt_bytes(desc->dtype);
+  const int32_t nsteps = (int32_t)sched.size();
+
+  // ready[t]: block of step t is in its slot; done[t]: step t's kernel finished with its slot
+  std::vector<hipEvent_t> ready(nsteps, nullptr), done(nsteps, nullptr);
+  hipError_t e = hipSuccess;
+  auto cleanup = [&]() {
+    for (auto ev : ready) if (ev) (void)hipEventDestroy(ev);
+    for (auto ev : done) if (ev) (void)hipEventDestroy(ev);
+  };
+  if (prefetch) {
+    for (int32_t t = 0; t < nsteps; ++t) {
+      if ((e = hipEventCreateWithFlags(&ready[t], hipEventDisableTiming)) != hipSuccess ||
+          (e = hipEventCreateWithFlags(&done[t], hipEventDisableTiming)) != hipSuccess) {
+        cleanup();
+        return hip_fail(e, "hipEventCreateWithFlags");
+      }
+    }
+  }
+  auto slot_k = [&](int32_t t) { return (void*)(ws + wl.slot_k[t & 1]); };
+  auto slot_v = [&](int32_t t) { return (void*)(ws + wl.slot_v[t & 1]); };
+  auto enqueue_copy = [&](int32_t t, hipStream_t s) -> hipError_t {
+    const int32_t j = sched[t];
+    hipError_t r = hipMemcpyAsync(slot_k(t), k_blocks[j], blk_bytes, hipMemcpyDeviceToDevice, s);
+    if (r == hipSuccess) r = hipMemcpyAsync(slot_v(t), v_blocks[j], blk_bytes, hipMemcpyDeviceToDevice, s);
+    return r;
+  };
+  // the copy stream starts after everything already queued on the compute stream (inputs ready)
+  hipEvent_t start_ev = nullptr;
+  if (prefetch && nsteps > 1) {
+    if ((e = hipEventCreateWithFlags(&start_ev, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventRecord(start_ev, cs)) != hipSuccess || (e = hipStreamWaitEvent(xs, start_ev, 0)) != hipSuccess) {
+      if (start_ev) (void)hipEventDestroy(start_ev);
+      cleanup();
+      return hip_fail(e, "copy stream start");
+    }
+    (void)hipEventDestroy(start_ev);
+    if ((e = enqueue_copy(1, xs)) != hipSuccess || (e = hipEventRecord(ready[1], xs)) != hipSuccess) {
+      cleanup();
+      return hip_fail(e, "ring receive copy");
+    }
+  }
+
+  for (int32_t t = 0; t < nsteps; ++t) {
+    const int32_t j = sched[t];
+    const void* kp = t == 0 ? k_blocks[j] : slot_k(t);
+    const void* vp = t == 0 ? v_blocks[j] : slot_v(t);
+    if (t > 0) {
+      if (prefetch) e = hipStreamWaitEvent(cs, ready[t], 0);
+      else e = enqueue_copy(t, cs);
+      if (e != hipSuccess) { cleanup(); return hip_fail(e, "ring receive"); }
+    }
+    BlockArgs a = block_args(desc, j, q, kp, vp);
+    const bool last = t == nsteps - 1;
+    a.flags = (t > 0 ? F_READ_STATE : 0) | (last ? F_WRITE_FINAL : F_WRITE_STATE);
+    a.st_o = (float*)(ws + wl.st_o);
+    a.st_m = (float*)(ws + wl.st_m);
+    a.st_l = (float*)(ws + wl.st_l);
+    a.out = out;
+    a.m_out = m_out;
+    a.l_out = l_out;
+    a.lse_out = lse_out;
+    const bool timed = prof && prof->used < (int32_t)prof->start.size();
+    if (timed && (e = hipEventRecord(prof->start[prof->used], cs)) != hipSuccess) { cleanup(); return hip_fail(e, "profiler record"); }
+    if ((e = launch_block(desc, a, cs)) != hipSuccess) { cleanup(); return hip_fail(e, "block kernel launch"); }
+    if (timed) {
+      if ((e = hipEventRecord(prof->stop[prof->used], cs)) != hipSuccess) { cleanup(); return hip_fail(e, "profiler record"); }
+      prof->used++;
+    }
+    if (prefetch && t + 1 < nsteps - 1) {
+      // the receive for step t+2 reuses the slot of step t: wait for this kernel
+      if ((e = hipEventRecord(done[t], cs)) != hipSuccess || (e = hipStreamWaitEvent(xs, done[t], 0)) != hipSuccess ||
+          (e = enqueue_copy(t + 2, xs)) != hipSuccess || (e = hipEventRecord(ready[t + 2], xs)) != hipSuccess) {
+        cleanup();
+        return hip_fail(e, "ring receive copy");
+      }
+    }
+  }
+  cleanup();
+  return CP_OK;
+}
+
+cp_status cp_attn_profiler_create(int32_t capacity, cp_attn_profiler** out) {
+  g_last_error.clear();
+  if (!out) return fail(CP_ERR_INVALID_ARG, "out is NULL");
+  if (capacity < 1 || capacity > (1 << 20)) return fail(CP_ERR_INVALID_ARG, "capacity=%d outside [1, 2^20]", capacity);
+  cp_attn_profiler* p = new (std::nothrow) cp_attn_profiler;
+  if (!p) return fail(CP_ERR_INVALID_ARG, "out of host memory");
+  p->start.assign(capacity, nullptr);
+  p->stop.assign(capacity, nullptr);
+  for (int32_t i = 0; i < capacity; ++i) {
+    hipError_t e = hipEventCreate(&p->start[i]);
+    if (e == hipSuccess) e = hipEventCreate(&p->stop[i]);
+    if (e != hipSuccess) {
+      cp_attn_profiler_destroy(p);
+      return hip_fail(e, "hipEventCreate");
+    }
+  }
+  *out = p;
+  return CP_OK;
+}
+
+cp_status cp_attn_profiler_reset(cp_attn_profiler* prof) {
+  g_last_error.clear();
+  if (!prof) return fail(CP_ERR_INVALID_ARG, "prof is NULL");
+  prof->used = 0;
+  return CP_OK;
+}
+
+cp_status cp_attn_profiler_read(cp_attn_profiler* prof, float* ms_out, int32_t capacity, int32_t* count_out) {
+  g_last_error.clear();
+  if (!prof || !count_out) return fail(CP_ERR_INVALID_ARG, "prof/count_out is NULL");
+  if (capacity < prof->used || (!ms_out && prof->used > 0))
+    return fail(CP_ERR_INVALID_ARG, "capacity %d < %d recorded launches", capacity, prof->used);
+  for (int32_t i = 0; i < prof->used; ++i) {
+    hipError_t e = hipEventSynchronize(prof->stop[i]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms_out[i], prof->start[i], prof->stop[i]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+  }
+  *count_out = prof->used;
+  return CP_OK;
+}
+
+void cp_attn_profiler_destroy(cp_attn_profiler* prof) {
+  if (!prof) return;
+  for (auto ev : prof->start) if (ev) (void)hipEventDestroy(ev);
+  for (auto ev : prof->stop) if (ev) (void)hipEventDestroy(ev);
+  delete prof;
+}
+
+}  // extern "C"

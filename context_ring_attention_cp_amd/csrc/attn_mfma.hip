@@ -1,0 +1,396 @@
+// bf16 block kernel for gfx950: one rank's query shard against one K/V block,
+// online softmax in registers, QK^T and PV on bf16 MFMA (fp32 accumulate).
+//
+// The recurrence is the one of the compassingai.com context-parallelism page,
+// section "線上 Softmax": per block S = Q K^T * scale, masked; row max; P =
+// exp(S - max); row sum; merge into the running (O, m, l) with the factor
+// exp(m_old - m_new).  Here it runs over key tiles of BN keys inside the block
+// as well, in base 2: scores are taken as x = s * scale * log2(e) and
+// exp(s*scale - m) = exp2(x - m*log2(e)).
+//
+// Work split: a workgroup of 4 waves owns BM = 128 query rows of one (batch,
+// head); each wave owns 32 rows.  Key tiles of BN = 64 keys of K and V are
+// staged through LDS (double buffered) and shared by the 4 waves.
+//
+// MFMA orientation (v_mfma_f32_32x32x16_bf16, D = A x B + C, A 32x16, B 16x32):
+//   S^T = K Q^T : A = K tile (rows = keys, k = head dim), B = Q^T (k = head
+//                 dim, columns = this wave's 32 queries).
+//   O^T = V^T P^T: A = V^T (rows = head dim, k = keys), B = P^T.
+// Every lane therefore holds one query column (lane % 32) of S^T and O^T: the
+// row max / row sum of the softmax are reductions over the lane's own
+// registers plus one exchange with lane ^ 32, and rescaling O is per lane.
+//
+// Operand layouts (lane l, g = l / 32, r = l % 32):
+//   A: lane holds A[r][8g .. 8g+7];  B: lane holds B[8g .. 8g+7][r];
+//   C/D: lane holds D[8(i/4) + 4g + i%4][r] for i = 0..15.
+// K rows are fed to A through pi(r) = r with bits 2 and 3 swapped, so that
+// accumulator element i of lane-half g belongs to key 16(i/8) + 8g + i%8 of
+// the 32-key sub-tile: elements 8h..8h+7 are then exactly the 8 consecutive
+// keys the B operand of the PV step with k-step 2t+h needs - P^T goes from
+// the S^T accumulator to the PV MFMA without any data movement.
+//
+// V^T comes from the row-major V tile in LDS through ds_read_b64_tr_b16:
+// within each group of 16 lanes, lane lam supplies the address of 4
+// consecutive elements of row base + lam/4 at column base + 4(lam%4) and
+// receives the elements at column base + lam of rows base .. base+3 -
+// 4 consecutive keys of one head-dim column.
+#include "kernels.h"
+
+#include <math.h>
+
+namespace cpattn {
+namespace {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int BM = 32 * kWaves;   // query rows per workgroup
+constexpr int BN = 64;            // keys per LDS tile
+constexpr float kLn2 = 0.693147180559945309417f;
+constexpr float kLog2e = 1.442695040888963407360f;
+
+// 16-byte chunk swizzles (XOR on the chunk index within a row).
+// K is read as MFMA A rows by 16 lanes at 16 different rows and one logical
+// chunk; V is read by the transpose loads at 4 rows x 4 chunks per 32 lanes.
+template <int D> __device__ __forceinline__ int swz_k(int row) {
+  if constexpr (D == 128) return row & 15;          // 256-B rows: chunk alone picks the bank
+  else return (row >> 1) & 7;                       // 128-B rows: row parity picks the half
+}
+template <int D> __device__ __forceinline__ int swz_v(int row) {
+  if constexpr (D == 128) return 4 * (row & 3);
+  else return 4 * ((row >> 1) & 1);
+}
+
+__device__ __forceinline__ int pi32(int r) {      // swap bits 2 and 3
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+__device__ __forceinline__ int64_t doc_start_of(const int32_t* __restrict__ cu, int ndocs, int64_t p) {
+  int lo = 0, hi = ndocs;                           // cu[lo] <= p < cu[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if ((int64_t)cu[mid] <= p) lo = mid; else hi = mid;
+  }
+  return cu[lo];
+}
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) {
+  constexpr int CH = D / 8;          // 16-byte chunks per row
+  constexpr int NS = D / 16;         // k-steps of S^T = K Q^T
+  constexpr int NDT = D / 32;        // 32-row tiles of O^T
+  constexpr int NT = BN / 32;        // 32-key sub-tiles of S^T
+  constexpr int NPV = BN / 16;       // k-steps of O^T = V^T P^T
+  constexpr int TILE = BN * D;       // elements of one K or V tile
+  constexpr int LOADS = BN * CH / kThreads;
+  static_assert(LOADS >= 1 && (BN * CH) % kThreads == 0, "tile load split");
+
+  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][TILE];   // [buffer][K, V]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int g = lane >> 5;
+  const int r32 = lane & 31;
+  const int64_t L = a.L;
+  const int H = a.H;
+
+  // Workgroup -> (batch, head, query tile).  Workgroups are dispatched to the
+  // 8 XCDs round robin; the remap gives each XCD a contiguous run of logical
+  // ids (one head's query tiles share its K/V in that XCD's L2).  Within a
+  // head, the query tiles that see the most keys start first.
+  const int nqt = (int)((L + BM - 1) / BM);
+  const int64_t nwg = (int64_t)nqt * H * a.B;
+  const int64_t bid = blockIdx.x;
+  const int64_t logical = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
+  const int64_t hb = logical / nqt;
+  const int qt = nqt - 1 - (int)(logical % nqt);
+  const int h = (int)(hb % H);
+  const int b = (int)(hb / H);
+
+  const int64_t rs = (int64_t)H * D;                        // row stride (elements)
+  const int64_t base = (int64_t)b * L * rs + (int64_t)h * D;
+  const bf16* __restrict__ qg = (const bf16*)a.q + base;
+  const bf16* __restrict__ kg = (const bf16*)a.k + base;
+  const bf16* __restrict__ vg = (const bf16*)a.v + base;
+
+  const int64_t q0 = (int64_t)qt * BM;
+  const int64_t qrow = q0 + 32 * w + r32;                   // this lane's query row
+  const bool row_ok = qrow < L;
+  const int64_t p = a.q_pos0 + qrow;                        // its global position
+  const int mask = a.mask;
+  const bool doc = mask == MASK_DOC_CAUSAL;
+
+  // Key tiles this workgroup needs.
+  const int nkt = (int)((L + BN - 1) / BN);
+  int kt_begin = 0, kt_end = nkt;
+  {
+    const int64_t wg_last = (q0 + BM < L ? q0 + BM : L) - 1;
+    if (mask != MASK_NONE) {
+      const int64_t hi = a.q_pos0 + wg_last - a.k_pos0;   // last visible key (local)
+      kt_end = hi < 0 ? 0 : (int)(hi / BN + 1 < nkt ? hi / BN + 1 : nkt);
+      if (doc) {
+        const int64_t lo = doc_start_of(a.cu, a.ndocs, a.q_pos0 + q0) - a.k_pos0;
+        if (lo > 0) kt_begin = (int)(lo / BN < nkt ? lo / BN : nkt);
+      }
+    }
+  }
+  const bool rd = a.flags & F_READ_STATE;
+  if (kt_begin >= kt_end && rd && !(a.flags & (F_WRITE_FINAL | F_WRITE_PARTIAL))) return;
+
+  // This wave's rows.
+  const int64_t w_first = q0 + 32 * w;
+  const bool wave_ok = w_first < L;
+  const int64_t w_last = (w_first + 31 < L ? w_first + 31 : L - 1);
+  const int64_t pw_first = a.q_pos0 + w_first, pw_last = a.q_pos0 + w_last;
+  int64_t ds_first = 0, ds_last = 0, dstart = 0;
+  if (doc && wave_ok) {
+    ds_first = doc_start_of(a.cu, a.ndocs, pw_first);
+    ds_last = doc_start_of(a.cu, a.ndocs, pw_last);
+    dstart = doc_start_of(a.cu, a.ndocs, row_ok ? p : pw_last);
+  }
+
+  // Q^T operand for this wave's 32 queries.
+  bf16x8 qreg[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (row_ok) qreg[s] = *(const bf16x8*)(qg + qrow * rs + 16 * s + 8 * g);
+    else qreg[s] = bf16x8{};
+  }
+
+  // Running state of this lane's query (m in base-2 units; l is this lane
+  // half's partial sum, combined with lane ^ 32 at the end).
+  floatx16 oacc[NDT];
+  float m_run = -INFINITY, l_run = 0.f;
+  const int64_t st_row = ((int64_t)b * L + qrow) * rs + (int64_t)h * D;   // element offset of [b][qrow][h][0]
+  const int64_t ml_idx = ((int64_t)b * H + h) * L + qrow;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = floatx16{};
+  if (rd && row_ok) {
+    m_run = a.st_m[ml_idx] * kLog2e;
+    l_run = g == 0 ? a.st_l[ml_idx] : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 v4 = *(const float4*)(a.st_o + st_row + 32 * dt + 8 * i4 + 4 * g);
+        oacc[dt][4 * i4 + 0] = v4.x;
+        oacc[dt][4 * i4 + 1] = v4.y;
+        oacc[dt][4 * i4 + 2] = v4.z;
+        oacc[dt][4 * i4 + 3] = v4.w;
+      }
+  }
+
+  const float c2 = a.scale_log2;
+
+  // Global -> register -> LDS staging of one K/V tile.
+  u32x4 kr[LOADS], vr[LOADS];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int u = tid + kThreads * i;
+      const int row = u / CH, c = u % CH;
+      const int64_t key = (int64_t)kt * BN + row;
+      if (key < L) {
+        kr[i] = *(const u32x4*)(kg + key * rs + 8 * c);
+        vr[i] = *(const u32x4*)(vg + key * rs + 8 * c);
+      } else {
+        kr[i] = u32x4{0u, 0u, 0u, 0u};
+        vr[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int u = tid + kThreads * i;
+      const int row = u / CH, c = u % CH;
+      *(u32x4*)(&smem[buf][0][row * D + 8 * (c ^ swz_k<D>(row))]) = kr[i];
+      *(u32x4*)(&smem[buf][1][row * D + 8 * (c ^ swz_v<D>(row))]) = vr[i];
+    }
+  };
+
+  // Lane constants of the LDS reads.
+  const int krow_l = pi32(r32);
+  const int tr_row = (lane & 15) >> 2;                       // + 16 kstep + 8 g + 4 h
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32 dt
+
+  auto compute = [&](int buf, int kt) {
+    const bf16* __restrict__ Ks = smem[buf][0];
+    const bf16* __restrict__ Vs = smem[buf][1];
+    floatx16 sacc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) sacc[t] = floatx16{};
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int row = 32 * t + krow_l;
+        const bf16x8 kv = *(const bf16x8*)(Ks + row * D + 8 * ((2 * s + g) ^ swz_k<D>(row)));
+        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qreg[s], sacc[t], 0, 0, 0);
+      }
+
+    // Mask: ragged tail, causal order, document boundaries.
+    const int64_t kbase = (int64_t)kt * BN;
+    const int64_t c_lo = a.k_pos0 + kbase;
+    const int64_t c_hi = a.k_pos0 + (kbase + BN < L ? kbase + BN : L) - 1;
+    const bool need_mask = (kbase + BN > L) ||
+                           (mask != MASK_NONE && (c_hi > pw_first || (doc && c_lo < ds_last)));
+    if (need_mask) {
+      // This lane's visible keys of the tile are the tile offsets [lo, hi]:
+      // below the ragged end, not after its query (causal), not before its
+      // document's first token.  Offsets are clamped to [-1, BN] before the
+      // narrowing so the comparisons stay in int32; the select is branch-free.
+      int64_t hi64 = (L - kbase < BN ? L - kbase : BN) - 1;
+      if (mask != MASK_NONE && p - c_lo < hi64) hi64 = p - c_lo;
+      int64_t lo64 = doc ? dstart - c_lo : 0;
+      const int hi = (int)(hi64 < -1 ? -1 : hi64) - 8 * g;
+      const int lo = (int)(lo64 < 0 ? 0 : (lo64 > BN ? BN : lo64)) - 8 * g;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ko = 32 * t + 16 * (i >> 3) + (i & 7);   // tile offset of element i, minus 8 g
+          sacc[t][i] = (ko >= lo && ko <= hi) ? sacc[t][i] : -INFINITY;
+        }
+    }
+
+    // Online softmax for this lane's query.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[t][i]);
+    mx = fmaxf(mx, xor32(mx));
+    const float m_new = fmaxf(m_run, mx * c2);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][i], c2, -m_use));
+        l_run += pv;
+        sacc[t][i] = pv;
+      }
+
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int ks = 0; ks < NPV; ++ks) {
+      const int t = ks >> 1, hh = ks & 1;
+      bf16x8 pb;
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const bf16x2 two = __builtin_convertvector(float2v{sacc[t][8 * hh + j], sacc[t][8 * hh + j + 1]}, bf16x2);
+        pb[j] = two[0];
+        pb[j + 1] = two[1];
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int col = 32 * dt + tr_col;
+        const int row0 = 16 * ks + 8 * g + tr_row;
+        const int row1 = row0 + 4;
+        const short4v x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4v*)(Vs + row0 * D + 8 * ((col >> 3) ^ swz_v<D>(row0)) + (col & 7)));
+        const short4v x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4v*)(Vs + row1 * D + 8 * ((col >> 3) ^ swz_v<D>(row1)) + (col & 7)));
+        const short8v x = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), pb, oacc[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  auto wave_skips = [&](int kt) -> bool {
+    if (mask == MASK_NONE) return false;
+    const int64_t kbase = (int64_t)kt * BN;
+    const int64_t c_lo = a.k_pos0 + kbase;
+    const int64_t c_hi = a.k_pos0 + (kbase + BN < L ? kbase + BN : L) - 1;
+    return c_lo > pw_last || (doc && c_hi < ds_first);
+  };
+
+  if (kt_begin < kt_end) {
+    load_tile(kt_begin);
+    store_tile(0);
+    __syncthreads();
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
+      const int buf = (kt - kt_begin) & 1;
+      const bool more = kt + 1 < kt_end;
+      if (more) load_tile(kt + 1);
+      if (wave_ok && !wave_skips(kt)) compute(buf, kt);
+      if (more) store_tile(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  if (!row_ok) return;
+  const float l_tot = l_run + xor32(l_run);
+  const bool has = l_tot > 0.f;
+
+  if (a.flags & F_WRITE_STATE) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *(float4*)(a.st_o + st_row + 32 * dt + 8 * i4 + 4 * g) =
+            float4{oacc[dt][4 * i4], oacc[dt][4 * i4 + 1], oacc[dt][4 * i4 + 2], oacc[dt][4 * i4 + 3]};
+    if (g == 0) {
+      a.st_m[ml_idx] = m_run * kLn2;
+      a.st_l[ml_idx] = l_tot;
+    }
+  }
+  const float inv = has ? 1.f / l_tot : 0.f;
+  const float lse = has ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+  if (a.flags & F_WRITE_FINAL) {
+    bf16* outp = (bf16*)a.out + st_row;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const bf16x2 lo2 = __builtin_convertvector(float2v{oacc[dt][4 * i4] * inv, oacc[dt][4 * i4 + 1] * inv}, bf16x2);
+        const bf16x2 hi2 = __builtin_convertvector(float2v{oacc[dt][4 * i4 + 2] * inv, oacc[dt][4 * i4 + 3] * inv}, bf16x2);
+        *(bf16x4*)(outp + 32 * dt + 8 * i4 + 4 * g) = bf16x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+      }
+    if (g == 0) {
+      if (a.m_out) a.m_out[ml_idx] = m_run * kLn2;
+      if (a.l_out) a.l_out[ml_idx] = l_tot;
+      if (a.lse_out) a.lse_out[ml_idx] = lse;
+    }
+  }
+  if (a.flags & F_WRITE_PARTIAL) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *(float4*)(a.o_part + st_row + 32 * dt + 8 * i4 + 4 * g) =
+            float4{oacc[dt][4 * i4] * inv, oacc[dt][4 * i4 + 1] * inv, oacc[dt][4 * i4 + 2] * inv,
+                   oacc[dt][4 * i4 + 3] * inv};
+    if (g == 0) a.lse_part[ml_idx] = lse;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_block_bf16(const BlockArgs& a, int d, hipStream_t s) {
+  const int64_t nqt = (a.L + BM - 1) / BM;
+  const int64_t nwg = nqt * a.H * a.B;
+  if (d == 128) attn_block_bf16_kernel<128><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
+  else attn_block_bf16_kernel<64><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace cpattn

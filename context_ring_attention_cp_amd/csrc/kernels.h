@@ -1,0 +1,80 @@
+// Internal interface between the host API (api.cpp) and the HIP kernels.
+// Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpattn {
+
+// What a block kernel reads and writes.
+enum : int32_t {
+  F_READ_STATE = 1,     // start from the running state (O, m, l) instead of empty
+  F_WRITE_STATE = 2,    // store the running state
+  F_WRITE_FINAL = 4,    // store out = O / l (input dtype) and m, l, lse
+  F_WRITE_PARTIAL = 8,  // store normalised O (float32) and lse of this block alone
+};
+
+enum : int32_t { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_DOC_CAUSAL = 2 };
+
+// One launch: the rank's query shard against one key/value block.
+struct BlockArgs {
+  const void* q;         // [B, L, H, d]
+  const void* k;         // [B, L, H, d] block j
+  const void* v;         // [B, L, H, d] block j
+  int64_t L;             // shard length (rows of q, rows of k/v)
+  int32_t B, H;
+  int64_t q_pos0;        // global position of query row 0 (rank * L)
+  int64_t k_pos0;        // global position of key row 0 (j * L)
+  int32_t mask;
+  int32_t ndocs;
+  const int32_t* cu;     // device cu_seqlens (DOC_CAUSAL)
+  float scale_log2;      // softmax scale * log2(e)
+  int32_t flags;
+  // running state
+  float* st_o;           // [B, L, H, d]
+  float* st_m;           // [B, H, L] natural-log units
+  float* st_l;           // [B, H, L]
+  // final outputs
+  void* out;             // [B, L, H, d] input dtype
+  float* m_out;          // [B, H, L] or null
+  float* l_out;
+  float* lse_out;
+  // partial outputs
+  float* o_part;         // [B, L, H, d]
+  float* lse_part;       // [B, H, L]
+};
+
+// Largest merge count handled by one kernel launch.
+constexpr int kMaxParts = 64;
+
+struct MergeArgs {
+  const float* o[kMaxParts];    // already in merge order
+  const float* lse[kMaxParts];
+  int32_t n;
+  int64_t L;
+  int32_t B, H, d;
+  int32_t out_bf16;
+  void* out;
+  float* lse_out;
+};
+
+struct FinalizeArgs {
+  const float* st_o;
+  const float* st_m;
+  const float* st_l;
+  int64_t L;
+  int32_t B, H, d;
+  int32_t out_bf16;
+  void* out;
+  float* m_out;
+  float* l_out;
+  float* lse_out;
+};
+
+// Launchers return the hipError_t of the launch.
+hipError_t launch_block_bf16(const BlockArgs& a, int d, hipStream_t s);
+hipError_t launch_block_f32(const BlockArgs& a, int d, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
+
+}  // namespace cpattn

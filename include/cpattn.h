@@ -1,0 +1,212 @@
+/*
+ * cpattn.h - C ABI of libcpattn: one context-parallel rank's share of ring
+ * attention on MI355X (gfx950).
+ *
+ * The operation (compassingai.com context-parallelism page, section "數學基礎"
+ * and section "線上 Softmax"): rank i of a ring of N holds the query shard
+ * Q_i of L = S/N contiguous tokens; it visits the key/value blocks K_j, V_j of
+ * every rank in ring order and keeps, per query row, a running max m, a
+ * running sum l and an unnormalised output O, merged block by block with the
+ * online-softmax recurrence; at the end O/l is the attention output and
+ * (m, l), lse = m + ln l are exported.  Masks: none (bidirectional), causal
+ * (key c visible to query p iff c <= p; blocks j > i are skipped and the
+ * diagonal block j = i is triangular - section "因果掩碼的特殊處理" of the same
+ * page) and packed documents with causal order (visible iff
+ * doc_start(p) <= c <= p, document boundaries kept across shards - the
+ * process-cxr.github.io page, sections "配置关注点" and "常见失败模式").
+ *
+ * Conventions for every entry point
+ *  - Tensors are caller-owned DEVICE memory, contiguous, row-major:
+ *      Q, K_j, V_j, out, O-state, partial O:   [B, L, H, d]
+ *      m, l, lse (state, outputs, partials):   [B, H, L]   (float32)
+ *    Q/K/V/out element type is desc->dtype (CP_F32: float32, CP_BF16:
+ *    bfloat16); running state, partial outputs, m, l and lse are float32.
+ *    Tensor base pointers must be 16-byte aligned; float32 vectors of
+ *    [B, H, L] must be 4-byte aligned.
+ *  - Host arrays (cu_seqlens, block pointer tables, merge order) are read
+ *    during the call only; the library keeps no pointer to them.
+ *  - Streams are hipStream_t passed as void* (NULL = the default stream).
+ *  - Calls are asynchronous: CP_OK means every argument was validated and the
+ *    work was enqueued.  All validation happens before anything is enqueued;
+ *    on a validation error nothing is enqueued.  A HIP launch failure returns
+ *    CP_ERR_HIP (work enqueued before it may remain in the stream).  Device
+ *    faults surface at the caller's next synchronisation.
+ *  - No exception or abort crosses the ABI.  On an error, cp_attn_last_error()
+ *    returns a message for the calling thread.
+ *  - The library allocates no device memory: scratch comes from the caller's
+ *    workspace (see cp_attn_workspace_bytes).
+ *
+ * Readings of points the pages leave open:
+ *  - the diagonal is visible under the causal mask (c <= p);
+ *  - a row that sees no key of a block has m = -inf, l = 0, lse = -inf and a
+ *    zero partial output; merging ignores it; finalising l = 0 gives O = 0;
+ *  - m is in natural-log units (the max of score * scale), l = sum exp(s - m);
+ *  - softmax scale defaults to 1/sqrt(d);
+ *  - cu_seqlens are global token positions over the whole sequence S = N L.
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CP_OK = 0,
+  CP_ERR_INVALID_ARG = 1,   /* a null/misaligned pointer, bad shape, bad index, malformed cu_seqlens */
+  CP_ERR_UNSUPPORTED = 2,   /* a valid request this build does not implement (e.g. d not in {64,128}) */
+  CP_ERR_WORKSPACE = 3,     /* workspace missing or smaller than cp_attn_workspace_bytes() */
+  CP_ERR_HIP = 4            /* a HIP runtime call failed; the message names it */
+} cp_status;
+
+typedef enum { CP_MASK_NONE = 0, CP_MASK_CAUSAL = 1, CP_MASK_DOC_CAUSAL = 2 } cp_mask;
+typedef enum { CP_F32 = 0, CP_BF16 = 1 } cp_dtype;
+
+/* Modes of cp_attn_block_partial. */
+typedef enum {
+  CP_MODE_INIT = 0,         /* state := (O, m, l) of this block alone */
+  CP_MODE_ACCUMULATE = 1,   /* state := online merge of state and this block */
+  CP_MODE_PARTIAL_LSE = 2   /* o_part := normalised O of this block alone, lse_part := its lse */
+} cp_block_mode;
+
+/* Flags of cp_attn_rank_forward. */
+#define CP_RING_PREFETCH 1  /* receive block t+1 on copy_stream while block t is computed */
+#define CP_RING_REVERSE 2   /* visit (i + t) mod N instead of (i - t) mod N */
+
+#define CP_MAX_RING 64      /* largest ring size N (and merge count n) accepted */
+
+/* Problem description (the shard statement of the pages: Q_i, K_j, V_j of
+ * shape (S/N) x H x d, rank i, ring size N, mask).  */
+typedef struct {
+  int32_t B;                     /* batch, >= 1 */
+  int32_t H;                     /* heads, >= 1 (same for Q and K/V) */
+  int32_t d;                     /* head dimension: 64 or 128 */
+  int32_t N;                     /* ring size, 1 <= N <= CP_MAX_RING */
+  int64_t L;                     /* shard length S/N, >= 1 */
+  int32_t rank;                  /* 0 <= rank < N: this shard's queries are tokens [rank L, (rank+1) L) */
+  int32_t dtype;                 /* cp_dtype of Q, K, V and out */
+  int32_t mask;                  /* cp_mask */
+  int32_t ndocs;                 /* DOC_CAUSAL only: number of documents */
+  const int32_t* cu_seqlens;     /* DOC_CAUSAL only: HOST array of ndocs+1 global boundaries,
+                                    cu[0] = 0 < cu[1] < ... < cu[ndocs] = N L */
+  const int32_t* cu_seqlens_dev; /* DOC_CAUSAL only: DEVICE copy of the same ndocs+1 values */
+  float scale;                   /* softmax scale; 0 means 1/sqrt(d) */
+} cp_attn_desc;
+
+/* Running state of one rank (device, float32): o unnormalised [B, L, H, d];
+ * m (natural-log units) and l [B, H, L]. */
+typedef struct {
+  float* o;
+  float* m;
+  float* l;
+} cp_state;
+
+/* Opaque per-launch timer (HIP events recorded around each attention kernel
+ * of cp_attn_rank_forward on the compute stream). */
+typedef struct cp_attn_profiler cp_attn_profiler;
+
+/* One block of the online-softmax recurrence (compassingai.com page, section
+ * "線上 Softmax": S_ij = Q_i K_j^T / sqrt(d), mask, m_ij, P_ij, l_ij, merge into
+ * (O, m, l)), run for block j (0 <= j < N) of the desc's ring.
+ *   q, k_j, v_j : device [B, L, H, d] of desc->dtype.
+ *   mode INIT/ACCUMULATE: `state` (device, caller-owned) is written (and read
+ *     for ACCUMULATE); o_part/lse_part must be NULL.
+ *   mode PARTIAL_LSE: o_part [B, L, H, d] and lse_part [B, H, L] (device
+ *     float32) receive the block's normalised output and lse; state must be
+ *     NULL.
+ * Rows with no visible key in the block: INIT sets m = -inf, l = 0, O = 0;
+ * ACCUMULATE leaves them unchanged; PARTIAL_LSE writes O = 0, lse = -inf.
+ * Errors: CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED, CP_ERR_HIP. */
+cp_status cp_attn_block_partial(const cp_attn_desc* desc, int32_t j, int32_t mode,
+                                const void* q, const void* k_j, const void* v_j,
+                                const cp_state* state, float* o_part, float* lse_part,
+                                void* stream);
+
+/* Merge of n per-block partials (O_j, lse_j) in the given order, the
+ * log-sum-exp form of the same recurrence: lse = ln sum_j exp(lse_j),
+ * O = sum_j exp(lse_j - lse) O_j (process-cxr.github.io page, section
+ * "Long Context Attention 中的通信": attention output aggregation with the
+ * softmax max/sum reductions).
+ *   o_parts, lse_parts : HOST arrays of n device pointers ([B, L, H, d] and
+ *                        [B, H, L] float32); 1 <= n <= CP_MAX_RING.
+ *   order              : HOST array of n distinct indices into the parts, or
+ *                        NULL for 0..n-1; terms are summed in this order.
+ *   out                : device [B, L, H, d] of desc->dtype;
+ *   lse_out            : device [B, H, L] float32, or NULL.
+ * Rows where every part is empty get O = 0 and lse = -inf.
+ * Errors: CP_ERR_INVALID_ARG, CP_ERR_HIP. */
+cp_status cp_attn_merge_lse(const cp_attn_desc* desc, int32_t n, const float* const* o_parts,
+                            const float* const* lse_parts, const int32_t* order, void* out,
+                            float* lse_out, void* stream);
+
+/* Final step of the recurrence: out = O / l (0 where l = 0) in desc->dtype
+ * (bf16 rounded to nearest even), and optionally m_out, l_out and
+ * lse_out = m + ln l (device [B, H, L] float32, each may be NULL).
+ * Errors: CP_ERR_INVALID_ARG, CP_ERR_HIP. */
+cp_status cp_attn_finalize(const cp_attn_desc* desc, const cp_state* state, void* out,
+                           float* m_out, float* l_out, float* lse_out, void* stream);
+
+/* Bytes of workspace cp_attn_rank_forward needs for this desc: two K/V
+ * receive slots, the running state and alignment padding.  Returns 0 if the
+ * desc is invalid (cp_attn_last_error() says why). */
+size_t cp_attn_workspace_bytes(const cp_attn_desc* desc);
+
+/* The whole forward of rank desc->rank (compassingai.com page, section
+ * "線上 Softmax", and the wangyu.me page, sections "Ring Attention" and
+ * "通信模式"), with the ring simulated on one GPU: K/V block j lives at
+ * k_blocks[j], v_blocks[j] (HOST arrays of N device pointers; the rank's own
+ * block is k_blocks[rank]).  At ring step t the rank holds block
+ * j_t = (rank - t) mod N (or (rank + t) mod N with CP_RING_REVERSE); blocks no
+ * row can see are skipped (causal: j > rank; documents: blocks that end before
+ * the document of the shard's first token begins).  Every step after the
+ * first receives its block into one of two workspace slots with a
+ * device-to-device copy; with CP_RING_PREFETCH the copy runs on copy_stream
+ * while the previous block is computed (events order slot reuse), otherwise
+ * it runs on compute_stream.  The last step writes the final output.
+ *   out          : device [B, L, H, d] of desc->dtype;
+ *   m_out, l_out, lse_out : device [B, H, L] float32, each may be NULL;
+ *   workspace    : device, >= cp_attn_workspace_bytes(desc) bytes, 256-byte
+ *                  aligned, not shared with a concurrent call;
+ *   copy_stream  : used only with CP_RING_PREFETCH; must differ from
+ *                  compute_stream; the function returns with all its work
+ *                  ordered before later work on compute_stream;
+ *   prof         : NULL, or a profiler that records each attention kernel.
+ * Errors: CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED, CP_ERR_WORKSPACE, CP_ERR_HIP. */
+cp_status cp_attn_rank_forward(const cp_attn_desc* desc, const void* q,
+                               const void* const* k_blocks, const void* const* v_blocks,
+                               void* out, float* m_out, float* l_out, float* lse_out,
+                               void* workspace, size_t workspace_bytes, void* compute_stream,
+                               void* copy_stream, int32_t flags, cp_attn_profiler* prof);
+
+/* Host-only: the blocks cp_attn_rank_forward computes on, in visiting order.
+ * Writes at most `capacity` block ids to blocks_out and the count to
+ * *count_out.  Errors: CP_ERR_INVALID_ARG (also when capacity is too small). */
+cp_status cp_attn_ring_schedule(const cp_attn_desc* desc, int32_t flags, int32_t* blocks_out,
+                                int32_t capacity, int32_t* count_out);
+
+/* Host-only: number of visible (query, key) pairs of ONE head of one batch
+ * element of this rank (causal-adjusted work is 4 d B H times this in
+ * flops).  Errors: CP_ERR_INVALID_ARG. */
+cp_status cp_attn_visible_pairs(const cp_attn_desc* desc, int64_t* pairs_out);
+
+/* Profiler: capacity = number of kernel launches it can time; records
+ * beyond capacity are dropped.  read() waits for the recorded events and
+ * writes each launch's duration in milliseconds; reset() forgets them. */
+cp_status cp_attn_profiler_create(int32_t capacity, cp_attn_profiler** out);
+cp_status cp_attn_profiler_reset(cp_attn_profiler* prof);
+cp_status cp_attn_profiler_read(cp_attn_profiler* prof, float* ms_out, int32_t capacity,
+                                int32_t* count_out);
+void cp_attn_profiler_destroy(cp_attn_profiler* prof);
+
+/* Static name of a status code. */
+const char* cp_attn_status_string(int32_t status);
+/* Message of the last error on the calling thread ("" if none). */
+const char* cp_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CPATTN_H */

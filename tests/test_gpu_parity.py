@@ -1,0 +1,305 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the
+same seeded inputs (bf16 inputs are handed to the oracle as the same
+bf16-rounded values).  Tolerances are in tests/gpu_util.py.
+
+Small cases span several query and key tiles with ragged tails (L not a
+multiple of any tile), batch > 1, every mask, both head dims and both input
+types, and are checked element by element on every rank.  The full-size
+workloads run in the launch configuration the benchmark times and are
+checked on sampled rows that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from harness.inputs import (TENSOR_K, TENSOR_Q, TENSOR_V, ShardSpec, draw_shard, make_inputs,
+                            normal_block, shuffled_order, standard_configs)
+from tests.gpu_util import check_o, check_stat, dev, host, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def cp():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import context_ring_attention_cp_amd as cp
+    cp.lib()     # raises if the library is not built: no fallback
+    return cp
+
+
+def _desc(cp, spec, rank, cu_dev=None, scale=0.0):
+    return cp.Desc(spec.B, spec.H, spec.d, spec.N, spec.L, rank, spec.dtype, spec.mask,
+                   cu_seqlens=spec.cu_seqlens, cu_seqlens_dev=cu_dev, scale=scale)
+
+
+def _outs(spec):
+    big = (spec.B, spec.L, spec.H, spec.d)
+    vec = (spec.B, spec.H, spec.L)
+    dt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+    return (torch.full(big, float("nan"), dtype=dt, device="cuda"),
+            torch.full(vec, float("nan"), device="cuda"), torch.full(vec, float("nan"), device="cuda"),
+            torch.full(vec, float("nan"), device="cuda"))
+
+
+def run_rank(cp, spec, rank, q, kb, vb, flags, scale=0.0):
+    """cp_attn_rank_forward on a fresh compute/copy stream pair."""
+    cu_dev = None
+    if spec.mask == "doc_causal":
+        cu_dev = torch.from_numpy(np.asarray(spec.cu_seqlens, np.int32)).cuda()
+    d = _desc(cp, spec, rank, cu_dev, scale)
+    out, m, l, lse = _outs(spec)
+    ws = cp.alloc_workspace(d)
+    cs, xs = torch.cuda.Stream(), torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        cp.cp_attn_rank_forward(d, q, kb, vb, out, m, l, lse, workspace=ws, compute_stream=cs,
+                                copy_stream=xs, flags=flags)
+    cs.synchronize()
+    torch.cuda.synchronize()
+    return host(out), host(m), host(l), host(lse)
+
+
+def _check_all(got, ref, dtype, rows=None, heads=None, rounding_floor=False):
+    o, m, l, lse = got
+    if rows is not None:
+        o = o[:, rows][:, :, heads]
+        m, l, lse = (x[:, heads][:, :, rows] for x in (m, l, lse))
+    stats = check_o(o, ref["o"], dtype, rounding_floor=rounding_floor)
+    check_stat(m, ref["m"], dtype, "m")
+    check_stat(l, ref["l"], dtype, "l")
+    check_stat(lse, ref["lse"], dtype, "lse")
+    return stats
+
+
+def _blocks(spec, inp):
+    return [dev(inp["k"][j], spec.dtype) for j in range(spec.N)], [dev(inp["v"][j], spec.dtype) for j in range(spec.N)]
+
+
+# ----------------------------------------------------------------------------
+# small cases, every rank, element by element
+
+
+def test_tiny_fp32_ring_all_ranks(cp):
+    """Four simulated ranks of S=1024 (H=2, d=64, fp32, causal) together give
+    full attention over the sequence."""
+    spec = standard_configs()[1]
+    inp = make_inputs(spec, seed=0, ranks=range(spec.N))
+    kb, vb = _blocks(spec, inp)
+    for r in range(spec.N):
+        say(f"[tiny fp32] rank {r}")
+        got = run_rank(cp, spec, r, dev(inp["q"][r], "f32"), kb, vb, cp.CP_RING_PREFETCH)
+        ref = oracle.rank_attention(inp["q"][r], inp["k"], inp["v"], r, spec.N, spec.mask)
+        _check_all(got, ref, "f32")
+
+
+def _small_cu(S):
+    pts, x = [0], 0
+    for n in (37, 130, 5, 300, 64, 1, 211, 90, 400):
+        x += n
+        if x >= S:
+            break
+        pts.append(x)
+    return np.asarray(pts + [S], np.int32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", ["none", "causal", "doc_causal"])
+def test_small_every_rank(cp, dtype, d, mask):
+    N, L, H, B = 3, 300, 2, 2
+    spec = ShardSpec(S=N * L, N=N, H=H, d=d, dtype=dtype, mask=mask, B=B, cfg_id=101,
+                     cu_seqlens=_small_cu(N * L) if mask == "doc_causal" else None)
+    inp = make_inputs(spec, seed=1, ranks=range(N))
+    kb, vb = _blocks(spec, inp)
+    for r in range(N):
+        say(f"[small] dtype={dtype} d={d} mask={mask} rank={r}")
+        got = run_rank(cp, spec, r, dev(inp["q"][r], dtype), kb, vb, cp.CP_RING_PREFETCH)
+        ref = oracle.rank_attention(inp["q"][r], inp["k"], inp["v"], r, N, mask, spec.cu_seqlens)
+        _check_all(got, ref, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_block_partial_modes_and_merge(cp, dtype):
+    """INIT / ACCUMULATE + finalize reproduce the rank's attention; each
+    PARTIAL_LSE block matches the oracle's per-block partial (including rows
+    with no visible key: lse = -inf, O = 0); merge_lse in a shuffled order
+    reproduces the rank's attention."""
+    N, L, H, d = 4, 200, 3, 128
+    spec = ShardSpec(S=N * L, N=N, H=H, d=d, dtype=dtype, mask="doc_causal", cfg_id=102,
+                     cu_seqlens=np.asarray([0, 90, 333, 450, 600, 601, 800], np.int32))
+    r = 2
+    inp = make_inputs(spec, seed=2, ranks=[r])
+    cu_dev = torch.from_numpy(spec.cu_seqlens).cuda()
+    desc = _desc(cp, spec, r, cu_dev)
+    q = dev(inp["q"][r], dtype)
+    kb, vb = _blocks(spec, inp)
+    big, vec = (1, L, H, d), (1, H, L)
+    ref = oracle.rank_attention(inp["q"][r], inp["k"], inp["v"], r, N, spec.mask, spec.cu_seqlens)
+
+    say(f"[modes] {dtype} init/accumulate/finalize")
+    st = (torch.zeros(big, device="cuda"), torch.zeros(vec, device="cuda"), torch.zeros(vec, device="cuda"))
+    for t, j in enumerate([2, 0, 3, 1]):
+        cp.cp_attn_block_partial(desc, j, cp.CP_MODE_INIT if t == 0 else cp.CP_MODE_ACCUMULATE, q, kb[j], vb[j],
+                                 state=st)
+    out, m, l, lse = _outs(spec)
+    cp.cp_attn_finalize(desc, st, out, m, l, lse)
+    torch.cuda.synchronize()
+    _check_all((host(out), host(m), host(l), host(lse)), ref, dtype)
+
+    say(f"[modes] {dtype} partial_lse + merge")
+    o_parts, lse_parts = [], []
+    for j in range(N):
+        op = torch.full(big, float("nan"), device="cuda")
+        lp = torch.full(vec, float("nan"), device="cuda")
+        cp.cp_attn_block_partial(desc, j, cp.CP_MODE_PARTIAL_LSE, q, kb[j], vb[j], o_part=op, lse_part=lp)
+        torch.cuda.synchronize()
+        bref = oracle.block_partial(inp["q"][r], inp["k"][j], inp["v"][j], r, j, N, spec.mask, spec.cu_seqlens)
+        check_o(host(op), bref["o"], dtype, what=f"o_part[{j}]")
+        check_stat(host(lp), bref["lse"], dtype, "lse")
+        o_parts.append(op)
+        lse_parts.append(lp)
+    out, _, _, lse = _outs(spec)
+    cp.cp_attn_merge_lse(desc, o_parts, lse_parts, [3, 1, 0, 2], out, lse)
+    torch.cuda.synchronize()
+    check_o(host(out), ref["o"], dtype)
+    check_stat(host(lse), ref["lse"], dtype, "lse")
+
+
+def test_prefetch_and_direction(cp):
+    """Prefetch on/off give bit-identical results (same kernels, same order);
+    the reversed ring order agrees within tolerance."""
+    spec = ShardSpec(S=4 * 512, N=4, H=2, d=128, dtype="bf16", mask="causal", cfg_id=103)
+    inp = make_inputs(spec, seed=3, ranks=[3])
+    kb, vb = _blocks(spec, inp)
+    q = dev(inp["q"][3], "bf16")
+    say("[ring] prefetch on/off, reverse")
+    a = run_rank(cp, spec, 3, q, kb, vb, cp.CP_RING_PREFETCH)
+    b = run_rank(cp, spec, 3, q, kb, vb, 0)
+    c = run_rank(cp, spec, 3, q, kb, vb, cp.CP_RING_PREFETCH | cp.CP_RING_REVERSE)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    ref = oracle.rank_attention(inp["q"][3], inp["k"], inp["v"], 3, 4, "causal")
+    _check_all(c, ref, "bf16")
+
+
+@pytest.mark.parametrize("mask", ["causal", "doc_causal"])
+def test_invisible_blocks_are_never_read(cp, mask):
+    """Blocks the schedule skips are filled with NaN: outputs stay finite and
+    bit-identical to a run with ordinary data there."""
+    N, L = 4, 256
+    cu = np.asarray([0, 100, 700, 900, 1024], np.int32)
+    spec = ShardSpec(S=N * L, N=N, H=2, d=128, dtype="bf16", mask=mask, cfg_id=104,
+                     cu_seqlens=cu if mask == "doc_causal" else None)
+    r = 3 if mask == "doc_causal" else 1
+    inp = make_inputs(spec, seed=4, ranks=[r])
+    kb, vb = _blocks(spec, inp)
+    q = dev(inp["q"][r], "bf16")
+    visited = set(oracle.ring_schedule(N, r, L, mask, spec.cu_seqlens))
+    assert len(visited) < N
+    say(f"[poison] {mask} rank {r} visits {sorted(visited)}")
+    a = run_rank(cp, spec, r, q, kb, vb, cp.CP_RING_PREFETCH)
+    kp = [k if j in visited else torch.full_like(k, float("nan")) for j, k in enumerate(kb)]
+    vp = [v if j in visited else torch.full_like(v, float("nan")) for j, v in enumerate(vb)]
+    b = run_rank(cp, spec, r, q, kp, vp, cp.CP_RING_PREFETCH)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    ref = oracle.rank_attention(inp["q"][r], inp["k"], inp["v"], r, N, mask, spec.cu_seqlens)
+    _check_all(a, ref, "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_degenerate_shapes(cp, dtype):
+    """L = 1 with N = 1 (one key: O = v_0), L = 1 with N = 5, an odd L with a
+    non-default softmax scale."""
+    for N, L, H, mask, scale in ((1, 1, 1, "causal", 0.0), (5, 1, 3, "causal", 0.0), (2, 77, 1, "none", 0.3),
+                                 (1, 129, 2, "causal", 0.05)):
+        say(f"[degenerate] {dtype} N={N} L={L} H={H} {mask} scale={scale}")
+        spec = ShardSpec(S=N * L, N=N, H=H, d=64, dtype=dtype, mask=mask, cfg_id=105)
+        inp = make_inputs(spec, seed=5, ranks=range(N))
+        kb, vb = _blocks(spec, inp)
+        for r in range(N):
+            got = run_rank(cp, spec, r, dev(inp["q"][r], dtype), kb, vb, cp.CP_RING_PREFETCH, scale=scale)
+            ref = oracle.rank_attention(inp["q"][r], inp["k"], inp["v"], r, N, mask,
+                                        scale=scale if scale > 0 else None)
+            _check_all(got, ref, dtype, rounding_floor=(L == 1))
+    spec = ShardSpec(S=1, N=1, H=1, d=64, dtype=dtype, mask="causal", cfg_id=106)
+    inp = make_inputs(spec, seed=6, ranks=[0])
+    kb, vb = _blocks(spec, inp)
+    o, m, l, lse = run_rank(cp, spec, 0, dev(inp["q"][0], dtype), kb, vb, 0)
+    assert np.allclose(o[0, 0, 0], inp["v"][0][0, 0, 0], atol=1e-2 if dtype == "bf16" else 1e-6)
+    assert abs(l[0, 0, 0] - 1.0) < 1e-6
+
+
+# ----------------------------------------------------------------------------
+# full-size workloads, sampled rows
+
+
+def _full_inputs(spec, seed, blocks):
+    q = draw_shard(spec, seed, TENSOR_Q, spec.rank)
+    k = {j: draw_shard(spec, seed, TENSOR_K, j) for j in blocks}
+    v = {j: draw_shard(spec, seed, TENSOR_V, j) for j in blocks}
+    return q, k, v
+
+
+def _heads(spec, seed):
+    rng = np.random.default_rng(seed + 17)
+    return sorted({0, spec.H - 1, int(rng.integers(spec.H))})
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 5])
+def test_full_size_rank_forward(cp, cfg):
+    """The causal 32K and 128K last-rank shards and the packed-document shard
+    at full size, ring prefetch on, sampled rows against the oracle."""
+    spec = standard_configs(seed=0)[cfg]
+    blocks = oracle.ring_schedule(spec.N, spec.rank, spec.L, spec.mask, spec.cu_seqlens)
+    say(f"[full cfg {cfg}] {spec.name}: blocks {blocks}")
+    q, k, v = _full_inputs(spec, 0, blocks)
+    kb = [dev(k[j], "bf16") if j in k else None for j in range(spec.N)]
+    vb = [dev(v[j], "bf16") if j in v else None for j in range(spec.N)]
+    got = run_rank(cp, spec, spec.rank, dev(q, "bf16"), kb, vb, cp.CP_RING_PREFETCH)
+    extra = []
+    if spec.cu_seqlens is not None:
+        s0 = spec.rank * spec.L
+        for x in spec.cu_seqlens:
+            if s0 <= x < s0 + spec.L:
+                extra += [x - s0 - 1, x - s0, x - s0 + 1]
+    rows = sample_rows(spec.L, cfg, extra=extra)
+    heads = _heads(spec, cfg)
+    ref = oracle.rank_attention(q, k, v, spec.rank, spec.N, spec.mask, spec.cu_seqlens, rows=rows, heads=heads)
+    stats = _check_all(got, ref, "bf16", rows=rows, heads=heads)
+    say(f"[full cfg {cfg}] {len(rows)} rows x {len(heads)} heads: {stats}")
+    for arr in got:
+        assert np.all(np.isfinite(arr))
+
+
+def test_full_size_partial_merge(cp):
+    """Bidirectional 64K over 8 ranks, rank 5, Q x 3: eight PARTIAL_LSE
+    blocks, then merge_lse in a seeded shuffled order; sampled rows."""
+    spec = standard_configs(seed=0)[4]
+    say(f"[full cfg 4] {spec.name}")
+    q, k, v = _full_inputs(spec, 0, range(spec.N))
+    desc = _desc(cp, spec, spec.rank)
+    qd = dev(q, "bf16")
+    big, vec = (1, spec.L, spec.H, spec.d), (1, spec.H, spec.L)
+    o_parts, lse_parts = [], []
+    for j in range(spec.N):
+        kd, vd = dev(k[j], "bf16"), dev(v[j], "bf16")
+        op = torch.empty(big, device="cuda")
+        lp = torch.empty(vec, device="cuda")
+        cp.cp_attn_block_partial(desc, j, cp.CP_MODE_PARTIAL_LSE, qd, kd, vd, o_part=op, lse_part=lp)
+        o_parts.append(op)
+        lse_parts.append(lp)
+    order = shuffled_order(0, 4, spec.N)
+    out, _, _, lse = _outs(spec)
+    cp.cp_attn_merge_lse(desc, o_parts, lse_parts, order, out, lse)
+    torch.cuda.synchronize()
+    rows = sample_rows(spec.L, 4)
+    heads = _heads(spec, 4)
+    ref = oracle.rank_attention(q, k, v, spec.rank, spec.N, spec.mask, rows=rows, heads=heads)
+    o = host(out)[:, rows][:, :, heads]
+    stats = check_o(o, ref["o"], "bf16")
+    check_stat(host(lse)[:, heads][:, :, rows], ref["lse"], "bf16", "lse")
+    say(f"[full cfg 4] order {order}: {stats}")
