@@ -4,13 +4,14 @@
 // The recurrence is the one of the compassingai.com context-parallelism page,
 // section "線上 Softmax": per block S = Q K^T * scale, masked; row max; P =
 // exp(S - max); row sum; merge into the running (O, m, l) with the factor
-// exp(m_old - m_new).  Here it runs over key tiles of BN keys inside the block
-// as well, in base 2: scores are taken as x = s * scale * log2(e) and
+// exp(m_old - m_new).  Here it also runs over key tiles of BN keys inside the
+// block, in base 2: scores are taken as x = s * scale * log2(e), and
 // exp(s*scale - m) = exp2(x - m*log2(e)).
 //
-// Work split: a workgroup of 4 waves owns BM = 128 query rows of one (batch,
-// head); each wave owns 32 rows.  Key tiles of BN = 64 keys of K and V are
-// staged through LDS (double buffered) and shared by the 4 waves.
+// Work split: a workgroup of 8 waves (two per SIMD) owns BM = 256 query rows
+// of one (batch, head); each wave owns 32 rows.  Key tiles of BN = 64 keys of
+// K and V are fetched straight into LDS (global_load_lds, 16 B per lane) in a
+// ring of 3 stages, one barrier per tile, and shared by the 8 waves.
 //
 // MFMA orientation (v_mfma_f32_32x32x16_bf16, D = A x B + C, A 32x16, B 16x32):
 //   S^T = K Q^T : A = K tile (rows = keys, k = head dim), B = Q^T (k = head
@@ -34,6 +35,16 @@
 // consecutive elements of row base + lam/4 at column base + 4(lam%4) and
 // receives the elements at column base + lam of rows base .. base+3 -
 // 4 consecutive keys of one head-dim column.
+//
+// Pipelining: the S^T MFMAs of tile t+1 are issued in the same basic block as
+// the softmax of tile t (independent work the scheduler interleaves), while
+// the DMA of tile t+2 is in flight.
+//
+// Lazy rescaling: the exponentials use a reference max m_ref that is only
+// raised (and O, l rescaled) when a tile's max exceeds it by more than 2^8;
+// P <= 256 in between.  O / l is unchanged by the choice of reference; at the
+// end O and l are rescaled once to the true running max, which is what the
+// state and the outputs hold.
 #include "kernels.h"
 
 #include <math.h>
@@ -49,14 +60,15 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef short short8v __attribute__((ext_vector_type(8)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int BM = 32 * kWaves;   // query rows per workgroup
 constexpr int BN = 64;            // keys per LDS tile
+constexpr int kStages = 3;        // LDS ring depth
 constexpr float kLn2 = 0.693147180559945309417f;
 constexpr float kLog2e = 1.442695040888963407360f;
+constexpr float kLazy = 8.0f;     // log2 headroom before a rescale
 
 // 16-byte chunk swizzles (XOR on the chunk index within a row).
 // K is read as MFMA A rows by 16 lanes at 16 different rows and one logical
@@ -85,6 +97,15 @@ __device__ __forceinline__ int64_t doc_start_of(const int32_t* __restrict__ cu, 
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// One 16-byte global -> LDS fetch per lane (global_load_lds_dwordx4): lane n's
+// data lands at dst + 16 n, dst wave-uniform.  Kept in a device function so
+// the host compilation pass of the kernel template never sees the builtin.
+__device__ __forceinline__ void fetch16(const bf16* src, lds_ptr dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) {
   constexpr int CH = D / 8;          // 16-byte chunks per row
@@ -93,10 +114,10 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   constexpr int NT = BN / 32;        // 32-key sub-tiles of S^T
   constexpr int NPV = BN / 16;       // k-steps of O^T = V^T P^T
   constexpr int TILE = BN * D;       // elements of one K or V tile
-  constexpr int LOADS = BN * CH / kThreads;
-  static_assert(LOADS >= 1 && (BN * CH) % kThreads == 0, "tile load split");
+  constexpr int DMA = BN * CH / kThreads;   // 16-byte fetches per lane per tensor per tile
+  static_assert(DMA >= 1 && (BN * CH) % kThreads == 0, "tile fetch split");
 
-  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][TILE];   // [buffer][K, V]
+  __shared__ __attribute__((aligned(16))) bf16 smem[kStages][2][TILE];   // [stage][K, V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -149,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   const bool rd = a.flags & F_READ_STATE;
   if (kt_begin >= kt_end && rd && !(a.flags & (F_WRITE_FINAL | F_WRITE_PARTIAL))) return;
 
-  // This wave's rows.
+  // This wave's rows and the key tiles it has to compute.
   const int64_t w_first = q0 + 32 * w;
   const bool wave_ok = w_first < L;
   const int64_t w_last = (w_first + 31 < L ? w_first + 31 : L - 1);
@@ -160,6 +181,17 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
     ds_last = doc_start_of(a.cu, a.ndocs, pw_last);
     dstart = doc_start_of(a.cu, a.ndocs, row_ok ? p : pw_last);
   }
+  int wkt_begin = kt_begin, wkt_end = wave_ok ? kt_end : kt_begin;
+  if (wave_ok && mask != MASK_NONE) {
+    const int64_t hi = pw_last - a.k_pos0;
+    const int e = hi < 0 ? 0 : (int)(hi / BN + 1 < nkt ? hi / BN + 1 : nkt);
+    if (e < wkt_end) wkt_end = e;
+    if (doc) {
+      const int64_t lo = ds_first - a.k_pos0;
+      const int bgn = lo <= 0 ? 0 : (int)(lo / BN < nkt ? lo / BN : nkt);
+      if (bgn > wkt_begin) wkt_begin = bgn;
+    }
+  }
 
   // Q^T operand for this wave's 32 queries.
   bf16x8 qreg[NS];
@@ -169,16 +201,16 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
     else qreg[s] = bf16x8{};
   }
 
-  // Running state of this lane's query (m in base-2 units; l is this lane
-  // half's partial sum, combined with lane ^ 32 at the end).
+  // Running state of this lane's query (base-2 units; l is this lane half's
+  // partial sum, combined with lane ^ 32 at the end).
   floatx16 oacc[NDT];
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_true = -INFINITY, m_ref = -INFINITY, l_run = 0.f;
   const int64_t st_row = ((int64_t)b * L + qrow) * rs + (int64_t)h * D;   // element offset of [b][qrow][h][0]
   const int64_t ml_idx = ((int64_t)b * H + h) * L + qrow;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = floatx16{};
   if (rd && row_ok) {
-    m_run = a.st_m[ml_idx] * kLog2e;
+    m_true = m_ref = a.st_m[ml_idx] * kLog2e;
     l_run = g == 0 ? a.st_l[ml_idx] : 0.f;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -194,42 +226,30 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
 
   const float c2 = a.scale_log2;
 
-  // Global -> register -> LDS staging of one K/V tile.
-  u32x4 kr[LOADS], vr[LOADS];
-  auto load_tile = [&](int kt) {
+  // Fetch key tile kt into LDS stage st: lane n of wave w's i-th fetch fills
+  // 16-byte slot (i * kThreads + 64 w + n) of the tile, i.e. row slot/CH,
+  // physical chunk slot%CH, which holds logical chunk phys ^ swizzle(row).
+  // Rows past the ragged end re-read row L-1 (finite data the mask drops).
+  auto fetch = [&](int kt, int st) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int u = tid + kThreads * i;
-      const int row = u / CH, c = u % CH;
-      const int64_t key = (int64_t)kt * BN + row;
-      if (key < L) {
-        kr[i] = *(const u32x4*)(kg + key * rs + 8 * c);
-        vr[i] = *(const u32x4*)(vg + key * rs + 8 * c);
-      } else {
-        kr[i] = u32x4{0u, 0u, 0u, 0u};
-        vr[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int u = tid + kThreads * i;
-      const int row = u / CH, c = u % CH;
-      *(u32x4*)(&smem[buf][0][row * D + 8 * (c ^ swz_k<D>(row))]) = kr[i];
-      *(u32x4*)(&smem[buf][1][row * D + 8 * (c ^ swz_v<D>(row))]) = vr[i];
+    for (int i = 0; i < DMA; ++i) {
+      const int slot = i * kThreads + tid;
+      const int row = slot / CH, phys = slot % CH;
+      int64_t key = (int64_t)kt * BN + row;
+      if (key > L - 1) key = L - 1;
+      const int wbase = (i * kThreads + 64 * w) * 8;        // element offset of the wave's 1 KiB run
+      fetch16(kg + key * rs + 8 * (phys ^ swz_k<D>(row)), (lds_ptr)(&smem[st][0][wbase]));
+      fetch16(vg + key * rs + 8 * (phys ^ swz_v<D>(row)), (lds_ptr)(&smem[st][1][wbase]));
     }
   };
 
   // Lane constants of the LDS reads.
   const int krow_l = pi32(r32);
-  const int tr_row = (lane & 15) >> 2;                       // + 16 kstep + 8 g + 4 h
+  const int tr_row = (lane & 15) >> 2;                         // + 16 kstep + 8 g + 4 h
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32 dt
 
-  auto compute = [&](int buf, int kt) {
-    const bf16* __restrict__ Ks = smem[buf][0];
-    const bf16* __restrict__ Vs = smem[buf][1];
-    floatx16 sacc[NT];
+  auto qk = [&](int st, floatx16 (&sacc)[NT]) {
+    const bf16* __restrict__ Ks = smem[st][0];
 #pragma unroll
     for (int t = 0; t < NT; ++t) sacc[t] = floatx16{};
 #pragma unroll
@@ -240,7 +260,9 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
         const bf16x8 kv = *(const bf16x8*)(Ks + row * D + 8 * ((2 * s + g) ^ swz_k<D>(row)));
         sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qreg[s], sacc[t], 0, 0, 0);
       }
+  };
 
+  auto softmax_pv = [&](int st, int kt, floatx16 (&sacc)[NT]) {
     // Mask: ragged tail, causal order, document boundaries.
     const int64_t kbase = (int64_t)kt * BN;
     const int64_t c_lo = a.k_pos0 + kbase;
@@ -254,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
       // narrowing so the comparisons stay in int32; the select is branch-free.
       int64_t hi64 = (L - kbase < BN ? L - kbase : BN) - 1;
       if (mask != MASK_NONE && p - c_lo < hi64) hi64 = p - c_lo;
-      int64_t lo64 = doc ? dstart - c_lo : 0;
+      const int64_t lo64 = doc ? dstart - c_lo : 0;
       const int hi = (int)(hi64 < -1 ? -1 : hi64) - 8 * g;
       const int lo = (int)(lo64 < 0 ? 0 : (lo64 > BN ? BN : lo64)) - 8 * g;
 #pragma unroll
@@ -271,15 +293,20 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[t][i]);
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[t][i], sacc[t][i + 1]));
     mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    l_run *= alpha;
+    const float mt = mx * c2;
+    m_true = fmaxf(m_true, mt);
+    const bool need = mt > m_ref + kLazy;
+    if (__any(need)) {
+      const float nref = need ? m_true : m_ref;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - nref) : 1.f;
+      m_ref = nref;
+      l_run *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+    }
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -290,6 +317,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
       }
 
     // O^T += V^T P^T.
+    const bf16* __restrict__ Vs = smem[st][1];
 #pragma unroll
     for (int ks = 0; ks < NPV; ++ks) {
       const int t = ks >> 1, hh = ks & 1;
@@ -315,31 +343,47 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
     }
   };
 
-  auto wave_skips = [&](int kt) -> bool {
-    if (mask == MASK_NONE) return false;
-    const int64_t kbase = (int64_t)kt * BN;
-    const int64_t c_lo = a.k_pos0 + kbase;
-    const int64_t c_hi = a.k_pos0 + (kbase + BN < L ? kbase + BN : L) - 1;
-    return c_lo > pw_last || (doc && c_hi < ds_first);
-  };
-
   if (kt_begin < kt_end) {
-    load_tile(kt_begin);
-    store_tile(0);
+    // Prologue: tiles kt_begin and kt_begin+1 in flight, the first resident.
+    fetch(kt_begin, 0);
+    if (kt_begin + 1 < kt_end) fetch(kt_begin + 1, 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-      const int buf = (kt - kt_begin) & 1;
-      const bool more = kt + 1 < kt_end;
-      if (more) load_tile(kt + 1);
-      if (wave_ok && !wave_skips(kt)) compute(buf, kt);
-      if (more) store_tile(buf ^ 1);
+    floatx16 sA[NT], sB[NT];
+    if (kt_begin >= wkt_begin && kt_begin < wkt_end) qk(0, sA);
+    int st_cur = 0, st_nxt = 1, st_fch = 2;
+    // One tile step: fetch t+2, S^T of t+1, softmax + PV of t, then barrier.
+    auto step = [&](int kt, floatx16 (&cur)[NT], floatx16 (&nxt)[NT]) {
+      if (kt + 2 < kt_end) fetch(kt + 2, st_fch);
+      if (kt + 1 < kt_end && kt + 1 >= wkt_begin && kt + 1 < wkt_end) qk(st_nxt, nxt);
+      if (kt >= wkt_begin && kt < wkt_end) softmax_pv(st_cur, kt, cur);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+      const int t0 = st_cur;
+      st_cur = st_nxt;
+      st_nxt = st_fch;
+      st_fch = t0;
+    };
+    int kt = kt_begin;
+    for (; kt + 1 < kt_end; kt += 2) {
+      step(kt, sA, sB);
+      step(kt + 1, sB, sA);
     }
+    if (kt < kt_end) step(kt, sA, sB);
+  }
+
+  // Rescale O and l from the reference max to the true running max.
+  if (m_true != -INFINITY && m_true != m_ref) {
+    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_true);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
   }
 
   if (!row_ok) return;
   const float l_tot = l_run + xor32(l_run);
   const bool has = l_tot > 0.f;
+  const float m_run = m_true;
 
   if (a.flags & F_WRITE_STATE) {
 #pragma unroll
@@ -354,6 +398,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
     }
   }
   const float inv = has ? 1.f / l_tot : 0.f;
+  // v_log_f32 is the base-2 logarithm
   const float lse = has ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   if (a.flags & F_WRITE_FINAL) {
     bf16* outp = (bf16*)a.out + st_row;
