@@ -21,6 +21,12 @@ LIB = os.path.join(PKG, "libcpattn.so")
 
 SOURCES = ["api.cpp", "attn_mfma.hip", "attn_f32.hip", "merge_finalize.hip"]
 
+# Per-source extra flags.  The bf16 block kernel takes maxima of MFMA results
+# and masked scores, which are never NaN: without NaN semantics the compiler
+# drops the canonicalising v_max that IEEE mode puts before every max.
+# Infinities keep their meaning (the masks use -inf).
+EXTRA = {"attn_mfma.hip": ["-fno-honor-nans"]}
+
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = [
@@ -34,7 +40,7 @@ COMMON = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in line)

@@ -3,7 +3,7 @@
 // (two receive slots, a copy stream, events).  Every public entry point
 // validates all of its arguments before it makes any HIP call, so invalid
 // calls fail without touching a device.
-#include "../../include/cpattn.h"
+#include "cpattn.h"
 #include "kernels.h"
 
 #include <hip/hip_runtime.h>

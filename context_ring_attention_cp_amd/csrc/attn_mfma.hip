@@ -11,7 +11,7 @@
 // Work split: a workgroup of 8 waves (two per SIMD) owns BM = 256 query rows
 // of one (batch, head); each wave owns 32 rows.  Key tiles of BN = 64 keys of
 // K and V are fetched straight into LDS (global_load_lds, 16 B per lane) in a
-// ring of 3 stages, one barrier per tile, and shared by the 8 waves.
+// ring of 3 stages and shared by the 8 waves.
 //
 // MFMA orientation (v_mfma_f32_32x32x16_bf16, D = A x B + C, A 32x16, B 16x32):
 //   S^T = K Q^T : A = K tile (rows = keys, k = head dim), B = Q^T (k = head
@@ -36,9 +36,8 @@
 // receives the elements at column base + lam of rows base .. base+3 -
 // 4 consecutive keys of one head-dim column.
 //
-// Pipelining: the S^T MFMAs of tile t+1 are issued in the same basic block as
-// the softmax of tile t (independent work the scheduler interleaves), while
-// the DMA of tile t+2 is in flight.
+// Overlap: the two waves of a SIMD belong to two groups that alternate MFMA
+// phases and softmax phases one phase apart (see the main loop).
 //
 // Lazy rescaling: the exponentials use a reference max m_ref that is only
 // raised (and O, l rescaled) when a tile's max exceeds it by more than 2^8;
@@ -95,9 +94,29 @@ __device__ __forceinline__ int64_t doc_start_of(const int32_t* __restrict__ cu, 
   return cu[lo];
 }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Value of lane ^ 32 (v_permlane32_swap exchanges the two 32-lane halves).
+__device__ __forceinline__ float xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  // r[0]: lanes 0-31 keep x, lanes 32-63 get lanes 0-31 of x; r[1]: lanes 0-31
+  // get lanes 32-63 of x, lanes 32-63 keep x.  The half that moved is the partner's.
+  const unsigned lo_half_kept = r[0], hi_half_moved = r[1];
+  const bool upper = (__lane_id() & 32) != 0;
+  return __builtin_bit_cast(float, upper ? lo_half_kept : hi_half_moved);
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Workgroup barrier that waits only for this wave's LDS reads (lgkmcnt(0)),
+// not for its in-flight global->LDS fetches: used where the fetched stage is
+// not read in the next phase.  The empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_read_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt and expcnt at their maximum, lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
 
 // One 16-byte global -> LDS fetch per lane (global_load_lds_dwordx4): lane n's
 // data lands at dst + 16 n, dst wave-uniform.  Kept in a device function so
@@ -114,8 +133,6 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   constexpr int NT = BN / 32;        // 32-key sub-tiles of S^T
   constexpr int NPV = BN / 16;       // k-steps of O^T = V^T P^T
   constexpr int TILE = BN * D;       // elements of one K or V tile
-  constexpr int DMA = BN * CH / kThreads;   // 16-byte fetches per lane per tensor per tile
-  static_assert(DMA >= 1 && (BN * CH) % kThreads == 0, "tile fetch split");
 
   __shared__ __attribute__((aligned(16))) bf16 smem[kStages][2][TILE];   // [stage][K, V]
 
@@ -170,27 +187,17 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   const bool rd = a.flags & F_READ_STATE;
   if (kt_begin >= kt_end && rd && !(a.flags & (F_WRITE_FINAL | F_WRITE_PARTIAL))) return;
 
-  // This wave's rows and the key tiles it has to compute.
+  // This wave's rows.  Every wave runs every key tile of the workgroup; tiles
+  // a wave cannot see are fully masked (only the few tiles of a causal
+  // diagonal band or a document edge).
   const int64_t w_first = q0 + 32 * w;
   const bool wave_ok = w_first < L;
   const int64_t w_last = (w_first + 31 < L ? w_first + 31 : L - 1);
   const int64_t pw_first = a.q_pos0 + w_first, pw_last = a.q_pos0 + w_last;
-  int64_t ds_first = 0, ds_last = 0, dstart = 0;
+  int64_t ds_last = 0, dstart = 0;
   if (doc && wave_ok) {
-    ds_first = doc_start_of(a.cu, a.ndocs, pw_first);
     ds_last = doc_start_of(a.cu, a.ndocs, pw_last);
     dstart = doc_start_of(a.cu, a.ndocs, row_ok ? p : pw_last);
-  }
-  int wkt_begin = kt_begin, wkt_end = wave_ok ? kt_end : kt_begin;
-  if (wave_ok && mask != MASK_NONE) {
-    const int64_t hi = pw_last - a.k_pos0;
-    const int e = hi < 0 ? 0 : (int)(hi / BN + 1 < nkt ? hi / BN + 1 : nkt);
-    if (e < wkt_end) wkt_end = e;
-    if (doc) {
-      const int64_t lo = ds_first - a.k_pos0;
-      const int bgn = lo <= 0 ? 0 : (int)(lo / BN < nkt ? lo / BN : nkt);
-      if (bgn > wkt_begin) wkt_begin = bgn;
-    }
   }
 
   // Q^T operand for this wave's 32 queries.
@@ -230,16 +237,40 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   // 16-byte slot (i * kThreads + 64 w + n) of the tile, i.e. row slot/CH,
   // physical chunk slot%CH, which holds logical chunk phys ^ swizzle(row).
   // Rows past the ragged end re-read row L-1 (finite data the mask drops).
-  auto fetch = [&](int kt, int st) {
+  // Tiles are fetched by the 256 lanes of waves 0-3 (the first wave group).
+  // Fetch i of a lane fills 16-byte slot (i * 256 + tid) of the tile: row
+  // i * RPS + tid / CH, physical chunk tid % CH.  The swizzles only use row
+  // bits below RPS, so every fetch of a lane reads the same logical chunk
+  // offset: one 32-bit byte offset per tensor and lane, plus a uniform tile and
+  // fetch offset.  Rows past the ragged end (last tile only) re-read row L-1
+  // (finite data the mask drops).
+  constexpr int kFetchThreads = kThreads / 2;
+  constexpr int DMA = BN * CH / kFetchThreads;   // 16-byte fetches per lane per tensor per tile
+  constexpr int RPS = kFetchThreads / CH;        // rows covered by one fetch of the 256 lanes
+  static_assert(DMA >= 1 && (BN * CH) % kFetchThreads == 0, "tile fetch split");
+  static_assert((D == 128 && RPS % 16 == 0) || (D == 64 && RPS % 16 == 0), "swizzle bits below RPS");
+  const int f_row = tid / CH;
+  const int f_ph = tid % CH;
+  const uint32_t fk_off = (uint32_t)(((int64_t)f_row * rs + 8 * (f_ph ^ swz_k<D>(f_row))) * 2);
+  const uint32_t fv_off = (uint32_t)(((int64_t)f_row * rs + 8 * (f_ph ^ swz_v<D>(f_row))) * 2);
+  auto fetch = [&](int kt, bf16* __restrict__ kd, bf16* __restrict__ vd) {
+    if ((int64_t)(kt + 1) * BN <= L) {
 #pragma unroll
-    for (int i = 0; i < DMA; ++i) {
-      const int slot = i * kThreads + tid;
-      const int row = slot / CH, phys = slot % CH;
-      int64_t key = (int64_t)kt * BN + row;
-      if (key > L - 1) key = L - 1;
-      const int wbase = (i * kThreads + 64 * w) * 8;        // element offset of the wave's 1 KiB run
-      fetch16(kg + key * rs + 8 * (phys ^ swz_k<D>(row)), (lds_ptr)(&smem[st][0][wbase]));
-      fetch16(vg + key * rs + 8 * (phys ^ swz_v<D>(row)), (lds_ptr)(&smem[st][1][wbase]));
+      for (int i = 0; i < DMA; ++i) {
+        const int64_t rowoff = ((int64_t)kt * BN + i * RPS) * rs;          // uniform
+        const int wbase = (i * kFetchThreads + 64 * w) * 8;
+        fetch16((const bf16*)((const char*)(kg + rowoff) + fk_off), (lds_ptr)(kd + wbase));
+        fetch16((const bf16*)((const char*)(vg + rowoff) + fv_off), (lds_ptr)(vd + wbase));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < DMA; ++i) {
+        int64_t key = (int64_t)kt * BN + i * RPS + f_row;
+        if (key > L - 1) key = L - 1;
+        const int wbase = (i * kFetchThreads + 64 * w) * 8;
+        fetch16(kg + key * rs + 8 * (f_ph ^ swz_k<D>(f_row)), (lds_ptr)(kd + wbase));
+        fetch16(vg + key * rs + 8 * (f_ph ^ swz_v<D>(f_row)), (lds_ptr)(vd + wbase));
+      }
     }
   };
 
@@ -248,53 +279,81 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   const int tr_row = (lane & 15) >> 2;                         // + 16 kstep + 8 g + 4 h
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32 dt
 
-  auto qk = [&](int st, floatx16 (&sacc)[NT]) {
-    const bf16* __restrict__ Ks = smem[st][0];
+  // S^T = K Q^T of one tile; the K operands of head-dim step s+2 are read
+  // while step s multiplies.
+  auto qk = [&](const bf16* __restrict__ Ks, floatx16 (&sacc)[NT]) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) sacc[t] = floatx16{};
+    auto rd = [&](int s, int t) {
+      const int row = 32 * t + krow_l;
+      return *(const bf16x8*)(Ks + row * D + 8 * ((2 * s + g) ^ swz_k<D>(row)));
+    };
+    bf16x8 kb[3][NT];
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+    for (int s = 0; s < 2 && s < NS; ++s)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int row = 32 * t + krow_l;
-        const bf16x8 kv = *(const bf16x8*)(Ks + row * D + 8 * ((2 * s + g) ^ swz_k<D>(row)));
-        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qreg[s], sacc[t], 0, 0, 0);
-      }
+      for (int t = 0; t < NT; ++t) kb[s][t] = rd(s, t);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (s + 2 < NS)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) kb[(s + 2) % 3][t] = rd(s + 2, t);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[s % 3][t], qreg[s], sacc[t], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NT, 0);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (s + 2 < NS) __builtin_amdgcn_sched_group_barrier(0x100, NT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);
+    }
   };
 
-  auto softmax_pv = [&](int st, int kt, floatx16 (&sacc)[NT]) {
-    // Mask: ragged tail, causal order, document boundaries.
+  // Mask of tile kt: ragged tail, causal order, document boundaries.
+  auto need_mask = [&](int kt) -> bool {
     const int64_t kbase = (int64_t)kt * BN;
     const int64_t c_lo = a.k_pos0 + kbase;
     const int64_t c_hi = a.k_pos0 + (kbase + BN < L ? kbase + BN : L) - 1;
-    const bool need_mask = (kbase + BN > L) ||
-                           (mask != MASK_NONE && (c_hi > pw_first || (doc && c_lo < ds_last)));
-    if (need_mask) {
-      // This lane's visible keys of the tile are the tile offsets [lo, hi]:
-      // below the ragged end, not after its query (causal), not before its
-      // document's first token.  Offsets are clamped to [-1, BN] before the
-      // narrowing so the comparisons stay in int32; the select is branch-free.
-      int64_t hi64 = (L - kbase < BN ? L - kbase : BN) - 1;
-      if (mask != MASK_NONE && p - c_lo < hi64) hi64 = p - c_lo;
-      const int64_t lo64 = doc ? dstart - c_lo : 0;
-      const int hi = (int)(hi64 < -1 ? -1 : hi64) - 8 * g;
-      const int lo = (int)(lo64 < 0 ? 0 : (lo64 > BN ? BN : lo64)) - 8 * g;
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ko = 32 * t + 16 * (i >> 3) + (i & 7);   // tile offset of element i, minus 8 g
-          sacc[t][i] = (ko >= lo && ko <= hi) ? sacc[t][i] : -INFINITY;
-        }
-    }
-
-    // Online softmax for this lane's query.
-    float mx = -INFINITY;
+    return (kbase + BN > L) || (mask != MASK_NONE && (c_hi > pw_first || (doc && c_lo < ds_last)));
+  };
+  auto apply_mask = [&](int kt, floatx16 (&sacc)[NT]) {
+    // This lane's visible keys of the tile are the tile offsets [lo, hi]:
+    // below the ragged end, not after its query (causal), not before its
+    // document's first token.  Offsets are clamped to [-1, BN] before the
+    // narrowing so the comparisons stay in int32; the select is branch-free.
+    const int64_t kbase = (int64_t)kt * BN;
+    const int64_t c_lo = a.k_pos0 + kbase;
+    int64_t hi64 = (L - kbase < BN ? L - kbase : BN) - 1;
+    if (mask != MASK_NONE && p - c_lo < hi64) hi64 = p - c_lo;
+    const int64_t lo64 = doc ? dstart - c_lo : 0;
+    const int hi = (int)(hi64 < -1 ? -1 : hi64) - 8 * g;
+    const int lo = (int)(lo64 < 0 ? 0 : (lo64 > BN ? BN : lo64)) - 8 * g;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[t][i], sacc[t][i + 1]));
-    mx = fmaxf(mx, xor32(mx));
+      for (int i = 0; i < 16; ++i) {
+        const int ko = 32 * t + 16 * (i >> 3) + (i & 7);   // tile offset of element i, minus 8 g
+        sacc[t][i] = (ko >= lo && ko <= hi) ? sacc[t][i] : -INFINITY;
+      }
+  };
+  // Row max of a tile (this lane's keys; both lane halves combined).
+  auto row_max = [&](floatx16 (&sacc)[NT]) -> float {
+    float m0 = fmaxf(sacc[0][0], sacc[0][1]), m1 = fmaxf(sacc[0][2], sacc[0][3]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = (t == 0 ? 4 : 0); i < 16; i += 4) {
+        m0 = fmaxf(m0, fmaxf(sacc[t][i], sacc[t][i + 1]));
+        m1 = fmaxf(m1, fmaxf(sacc[t][i + 2], sacc[t][i + 3]));
+      }
+    const float mx = fmaxf(m0, m1);
+    return fmaxf(mx, xor32(mx));
+  };
+  // Lazy rescale for a tile with row max mx (raw score units): raise the
+  // reference max, and rescale O and l, only when the tile's max exceeds it
+  // by more than kLazy (wave-uniform branch, rarely taken).
+  auto rescale = [&](float mx) {
     const float mt = mx * c2;
     m_true = fmaxf(m_true, mt);
     const bool need = mt > m_ref + kLazy;
@@ -306,28 +365,41 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
     }
+  };
+  // P = exp2(x - m_ref) of a tile, in place, summed into l; returns P packed
+  // to bf16 as the four PV B operands.
+  auto exp_sum = [&](floatx16 (&sacc)[NT], bf16x8 (&pb)[NPV]) {
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][i], c2, -m_use));
-        l_run += pv;
-        sacc[t][i] = pv;
-      }
-
-    // O^T += V^T P^T.
-    const bf16* __restrict__ Vs = smem[st][1];
+      for (int i = 0; i < 16; ++i) sacc[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][i], c2, -m_use));
+    float part[NT * 4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        part[4 * t + q] = (sacc[t][4 * q] + sacc[t][4 * q + 1]) + (sacc[t][4 * q + 2] + sacc[t][4 * q + 3]);
+#pragma unroll
+    for (int n = NT * 4; n > 1; n /= 2)
+#pragma unroll
+      for (int q = 0; q < n / 2; ++q) part[q] = part[2 * q] + part[2 * q + 1];
+    l_run += part[0];
 #pragma unroll
     for (int ks = 0; ks < NPV; ++ks) {
       const int t = ks >> 1, hh = ks & 1;
-      bf16x8 pb;
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
         const bf16x2 two = __builtin_convertvector(float2v{sacc[t][8 * hh + j], sacc[t][8 * hh + j + 1]}, bf16x2);
-        pb[j] = two[0];
-        pb[j + 1] = two[1];
+        pb[ks][j] = two[0];
+        pb[ks][j + 1] = two[1];
       }
+    }
+  };
+  // O^T += V^T P^T for one tile.
+  auto pv = [&](const bf16* __restrict__ Vs, bf16x8 (&pb)[NPV]) {
+#pragma unroll
+    for (int ks = 0; ks < NPV; ++ks)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const int col = 32 * dt + tr_col;
@@ -338,38 +410,53 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
         const short4v x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) short4v*)(Vs + row1 * D + 8 * ((col >> 3) ^ swz_v<D>(row1)) + (col & 7)));
         const short8v x = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), pb, oacc[dt], 0, 0, 0);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), pb[ks], oacc[dt], 0, 0, 0);
       }
-    }
   };
 
   if (kt_begin < kt_end) {
-    // Prologue: tiles kt_begin and kt_begin+1 in flight, the first resident.
-    fetch(kt_begin, 0);
-    if (kt_begin + 1 < kt_end) fetch(kt_begin + 1, 1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    floatx16 sA[NT], sB[NT];
-    if (kt_begin >= wkt_begin && kt_begin < wkt_end) qk(0, sA);
-    int st_cur = 0, st_nxt = 1, st_fch = 2;
-    // One tile step: fetch t+2, S^T of t+1, softmax + PV of t, then barrier.
-    auto step = [&](int kt, floatx16 (&cur)[NT], floatx16 (&nxt)[NT]) {
-      if (kt + 2 < kt_end) fetch(kt + 2, st_fch);
-      if (kt + 1 < kt_end && kt + 1 >= wkt_begin && kt + 1 < wkt_end) qk(st_nxt, nxt);
-      if (kt >= wkt_begin && kt < wkt_end) softmax_pv(st_cur, kt, cur);
+    // Two wave groups per SIMD play ping-pong: group 0 (waves 0-3) and group 1
+    // (waves 4-7) alternate a compute phase (S^T MFMAs of tile u, PV MFMAs of
+    // tile u-1) with a softmax phase (mask, max, rescale, exponentials, sums,
+    // bf16 packing of tile u), one phase apart, with a workgroup barrier at
+    // every phase boundary - while one wave of a SIMD keeps the matrix core
+    // busy the other uses the vector ALU.
+    //
+    // Tile u lives in LDS stage (u - kt_begin) % 3.  Group 0 fetches tile u+1
+    // at the start of its softmax phase of tile u, into the stage of tile u-2
+    // (whose V was last read in group 1's compute phase of tile u-1, two
+    // phases earlier), and waits for it at the end of that phase, before the
+    // barrier that precedes both groups' first use of it.
+    const int grp = w >> 2;
+    auto stage = [&](int u) { return (u - kt_begin) % kStages; };
+    if (grp == 0) {
+      fetch(kt_begin, smem[0][0], smem[0][1]);
       __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      const int t0 = st_cur;
-      st_cur = st_nxt;
-      st_nxt = st_fch;
-      st_fch = t0;
-    };
-    int kt = kt_begin;
-    for (; kt + 1 < kt_end; kt += 2) {
-      step(kt, sA, sB);
-      step(kt + 1, sB, sA);
     }
-    if (kt < kt_end) step(kt, sA, sB);
+    __syncthreads();
+    if (grp == 1) __syncthreads();                   // group 1 runs one phase behind
+    floatx16 sacc[NT];
+    bf16x8 pb[NPV];
+    for (int u = kt_begin; u <= kt_end; ++u) {
+      // compute phase
+      if (u < kt_end) qk(smem[stage(u)][0], sacc);
+      if (u > kt_begin) pv(smem[stage(u - 1)][1], pb);
+      lds_read_barrier();
+      // softmax phase (group 0 also starts the fetch of tile u+1: this phase
+      // reads no LDS, so nothing in it waits for the fetch)
+      if (grp == 0 && u + 1 < kt_end) {
+        const int sf = stage(u + 1);
+        fetch(u + 1, smem[sf][0], smem[sf][1]);
+      }
+      if (u < kt_end) {
+        if (need_mask(u)) apply_mask(u, sacc);
+        rescale(row_max(sacc));
+        exp_sum(sacc, pb);
+      }
+      if (grp == 0) __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    if (grp == 0) __syncthreads();                   // same barrier count for both groups
   }
 
   // Rescale O and l from the reference max to the true running max.
