@@ -13,6 +13,9 @@ Prints ONE JSON line.  The metric is causal-adjusted attention TFLOP/s:
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +29,67 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk (the published 2.5 PF)
 PEAK_HBM_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "context_ring_attention_cp_amd", "csrc", "attn_mfma.hip")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "attn_block_bf16__causal_128k_last_rank.traffic.json")
+ATTN_KERNEL = "attn_block_bf16_kernel<128>"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def kernel_sha256() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _pmc_rows(d: str, counter: str):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    return sorted(rows)
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int, out: str) -> dict:
+    """HBM traffic of the attention kernel from a FETCH_SIZE run and a
+    WRITE_SIZE run (KiB per dispatch) of `bench.py --steps 1 --warmup 0`.
+    Each counter is scaled by what it reads for the ring-receive copy kernels
+    of the same run, which move `copy_bytes` each (one K or V block)."""
+    res = {}
+    for name, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _pmc_rows(d, counter)
+        cal = [v for _, k, v in rows if COPY_KERNEL in k and abs(v * 1024 - copy_bytes) < 0.6 * copy_bytes]
+        att = [v for _, k, v in rows if ATTN_KERNEL in k]
+        if not cal or not att:
+            raise SystemExit(f"{counter}: calibration copies {len(cal)}, attention dispatches {len(att)}")
+        factor = copy_bytes / (sum(cal) / len(cal) * 1024)
+        res[name] = {"counter": counter, "kib_per_dispatch": att, "copy_kib": sum(cal) / len(cal), "factor": factor}
+    n = min(len(res["fetch"]["kib_per_dispatch"]), len(res["write"]["kib_per_dispatch"]))
+    per = [res["fetch"]["kib_per_dispatch"][i] * 1024 * res["fetch"]["factor"]
+           + res["write"]["kib_per_dispatch"][i] * 1024 * res["write"]["factor"] for i in range(n)]
+    summary = {"kernel": ATTN_KERNEL, "kernel_source_sha256": kernel_sha256(), "dispatches": n,
+               "traffic_bytes_per_dispatch": per, "traffic_bytes_mean": sum(per) / n,
+               "fetch": res["fetch"], "write": res["write"], "calibration_copy_bytes": copy_bytes,
+               "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o <name> -- "
+                          "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline"}
+    with open(out, "w") as f:
+        json.dump(summary, f, indent=1)
+    return summary
+
+
+def measured_traffic():
+    """Mean HBM bytes per attention dispatch from the committed PMC summary,
+    or None if it was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_sha256():
+        return None
+    return t["traffic_bytes_mean"]
 
 
 def parse():
@@ -37,6 +101,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="query rows of one head timed on the CPU oracle")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic summary from two rocprofv3 --pmc runs and exit (no GPU)")
     return ap.parse_args()
 
 
@@ -69,6 +135,10 @@ def cpu_baseline(spec, q, k, v, rows_n: int):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        blk = 32768 * 32 * 128 * 2          # one K or V block of the 128K example, bf16
+        print(json.dumps(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], blk, TRAFFIC_JSON)))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -134,6 +204,7 @@ def main():
     k_sum = sum(kernel_ms)
     achieved = flops * args.steps / (k_sum * 1e-3) / 1e12
     per_step = [kernel_ms[i:i + len(sched)] for i in range(0, len(kernel_ms), len(sched))]
+    traffic = measured_traffic()
     blk_bytes = spec.B * L * H * d * 2
     res = {
         "metric": "causal-adjusted attention TFLOP/s per rank shard; % of MI355X bf16 MFMA peak",
@@ -154,7 +225,7 @@ def main():
                    "seed": args.seed},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "flops_per_step": flops,
         "kernel_ms_per_step": [round(x, 4) for x in per_step[-1]] if per_step else [],
         "kernel_mean_ms": round(k_sum / max(1, len(kernel_ms)), 4),
