@@ -64,7 +64,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int BM = 32 * kWaves;   // query rows per workgroup
 constexpr int BN = 64;            // keys per LDS tile
-constexpr int kStages = 3;        // LDS ring depth
+constexpr int kStages = 4;        // LDS ring depth
 constexpr float kLn2 = 0.693147180559945309417f;
 constexpr float kLog2e = 1.442695040888963407360f;
 constexpr float kLazy = 8.0f;     // log2 headroom before a rescale
@@ -119,10 +119,18 @@ __device__ __forceinline__ void lds_read_barrier() {
 }
 
 // One 16-byte global -> LDS fetch per lane (global_load_lds_dwordx4): lane n's
-// data lands at dst + 16 n, dst wave-uniform.  Kept in a device function so
-// the host compilation pass of the kernel template never sees the builtin.
-__device__ __forceinline__ void fetch16(const bf16* src, lds_ptr dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+// data lands at lds + 16 n (lds wave-uniform, through M0), read from
+// base + off (base wave-uniform, off per lane).  Written as inline assembly so
+// that the compiler does not track it: the kernel itself waits for the fetches
+// (vmcnt) before the barrier that publishes a stage, and the compiler
+// therefore never places a full vmcnt(0) wait in front of LDS reads of other
+// stages.
+__device__ __forceinline__ void fetch16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+               "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 template <int D>
@@ -253,14 +261,14 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   const int f_ph = tid % CH;
   const uint32_t fk_off = (uint32_t)(((int64_t)f_row * rs + 8 * (f_ph ^ swz_k<D>(f_row))) * 2);
   const uint32_t fv_off = (uint32_t)(((int64_t)f_row * rs + 8 * (f_ph ^ swz_v<D>(f_row))) * 2);
-  auto fetch = [&](int kt, bf16* __restrict__ kd, bf16* __restrict__ vd) {
+  auto fetch = [&](int kt, bf16* kd, bf16* vd) {
     if ((int64_t)(kt + 1) * BN <= L) {
 #pragma unroll
       for (int i = 0; i < DMA; ++i) {
         const int64_t rowoff = ((int64_t)kt * BN + i * RPS) * rs;          // uniform
         const int wbase = (i * kFetchThreads + 64 * w) * 8;
-        fetch16((const bf16*)((const char*)(kg + rowoff) + fk_off), (lds_ptr)(kd + wbase));
-        fetch16((const bf16*)((const char*)(vg + rowoff) + fv_off), (lds_ptr)(vd + wbase));
+        fetch16(kg + rowoff, fk_off, lds_addr(kd + wbase));
+        fetch16(vg + rowoff, fv_off, lds_addr(vd + wbase));
       }
     } else {
 #pragma unroll
@@ -268,8 +276,8 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
         int64_t key = (int64_t)kt * BN + i * RPS + f_row;
         if (key > L - 1) key = L - 1;
         const int wbase = (i * kFetchThreads + 64 * w) * 8;
-        fetch16(kg + key * rs + 8 * (f_ph ^ swz_k<D>(f_row)), (lds_ptr)(kd + wbase));
-        fetch16(vg + key * rs + 8 * (f_ph ^ swz_v<D>(f_row)), (lds_ptr)(vd + wbase));
+        fetch16(kg, (uint32_t)((key * rs + 8 * (f_ph ^ swz_k<D>(f_row))) * 2), lds_addr(kd + wbase));
+        fetch16(vg, (uint32_t)((key * rs + 8 * (f_ph ^ swz_v<D>(f_row))) * 2), lds_addr(vd + wbase));
       }
     }
   };
@@ -415,24 +423,14 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   };
 
   if (kt_begin < kt_end) {
-    // Two wave groups per SIMD play ping-pong: group 0 (waves 0-3) and group 1
-    // (waves 4-7) alternate a compute phase (S^T MFMAs of tile u, PV MFMAs of
-    // tile u-1) with a softmax phase (mask, max, rescale, exponentials, sums,
-    // bf16 packing of tile u), one phase apart, with a workgroup barrier at
-    // every phase boundary - while one wave of a SIMD keeps the matrix core
-    // busy the other uses the vector ALU.
-    //
-    // Tile u lives in LDS stage (u - kt_begin) % 3.  Group 0 fetches tile u+1
-    // at the start of its softmax phase of tile u, into the stage of tile u-2
-    // (whose V was last read in group 1's compute phase of tile u-1, two
-    // phases earlier), and waits for it at the end of that phase, before the
-    // barrier that precedes both groups' first use of it.
     const int grp = w >> 2;
-    auto stage = [&](int u) { return (u - kt_begin) % kStages; };
+    auto stage = [&](int u) { return (u - kt_begin) & (kStages - 1); };
     if (grp == 0) {
       fetch(kt_begin, smem[0][0], smem[0][1]);
-      __builtin_amdgcn_s_waitcnt(0);
+      if (kt_begin + 1 < kt_end) fetch(kt_begin + 1, smem[1][0], smem[1][1]);
     }
+    // every wave: the first two tiles (group 0) and the Q / state loads are done
+    __builtin_amdgcn_s_waitcnt(0x0070);              // vmcnt(0) lgkmcnt(0)
     __syncthreads();
     if (grp == 1) __syncthreads();                   // group 1 runs one phase behind
     floatx16 sacc[NT];
@@ -442,19 +440,23 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
       if (u < kt_end) qk(smem[stage(u)][0], sacc);
       if (u > kt_begin) pv(smem[stage(u - 1)][1], pb);
       lds_read_barrier();
-      // softmax phase (group 0 also starts the fetch of tile u+1: this phase
-      // reads no LDS, so nothing in it waits for the fetch)
-      if (grp == 0 && u + 1 < kt_end) {
-        const int sf = stage(u + 1);
-        fetch(u + 1, smem[sf][0], smem[sf][1]);
+      // softmax phase; group 0 first starts the fetch of tile u+2
+      const bool more = u + 2 < kt_end;
+      if (grp == 0 && more) {
+        const int sf = stage(u + 2);
+        fetch(u + 2, smem[sf][0], smem[sf][1]);
       }
       if (u < kt_end) {
         if (need_mask(u)) apply_mask(u, sacc);
         rescale(row_max(sacc));
         exp_sum(sacc, pb);
       }
-      if (grp == 0) __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      // tile u+1 must have landed: at most the fetch of tile u+2 outstanding
+      __asm__ volatile("" ::: "memory");
+      if (more) __builtin_amdgcn_s_waitcnt(D == 128 ? 0x0078 : 0x0074);   // vmcnt(8 or 4) lgkmcnt(0)
+      else __builtin_amdgcn_s_waitcnt(0x0070);                             // vmcnt(0) lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
     }
     if (grp == 0) __syncthreads();                   // same barrier count for both groups
   }
