@@ -73,7 +73,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int, out: str) -> 
                "traffic_bytes_per_dispatch": per, "traffic_bytes_mean": sum(per) / n,
                "fetch": res["fetch"], "write": res["write"], "calibration_copy_bytes": copy_bytes,
                "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o <name> -- "
-                          "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline"}
+                          "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-secondary"}
     with open(out, "w") as f:
         json.dump(summary, f, indent=1)
     return summary
@@ -99,6 +99,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the brief timing of the other workloads")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="query rows of one head timed on the CPU oracle")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -131,6 +133,90 @@ def cpu_baseline(spec, q, k, v, rows_n: int):
             "sample": f"{rows_n} evenly spaced query rows of head 0 of 32 ({pairs} visible pairs, "
                       f"{dt:.1f} s wall, fp64 numpy, materialised score rows)",
             "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def _timed(fn, stream, warmup: int, reps: int) -> float:
+    """Mean milliseconds of fn() over `reps` runs on `stream` (HIP events)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def secondary(seed: int, reps: int = 5):
+    """The other workloads of the path, timed briefly: the causal 32K
+    last-rank shard, the packed-document shard (rank_forward, ring prefetch),
+    and the bidirectional 64K merge stress case (8 PARTIAL_LSE launches, then
+    one merge in a shuffled order; the merge is reported against HBM)."""
+    import torch
+
+    import context_ring_attention_cp_amd as cp
+    from harness.inputs import TENSOR_K, TENSOR_Q, TENSOR_V, bf16_bits, draw_shard, shuffled_order, standard_configs
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(bf16_bits(x)).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+    out = {}
+    cfgs = standard_configs(seed)
+    cs, xs = torch.cuda.Stream(), torch.cuda.Stream()
+    for cfg in (2, 5):
+        spec = cfgs[cfg]
+        cu_dev = None if spec.cu_seqlens is None else torch.from_numpy(spec.cu_seqlens).to("cuda")
+        desc = cp.Desc(spec.B, spec.H, spec.d, spec.N, spec.L, spec.rank, "bf16", spec.mask,
+                       cu_seqlens=spec.cu_seqlens, cu_seqlens_dev=cu_dev)
+        sched = cp.cp_attn_ring_schedule(desc, cp.CP_RING_PREFETCH)
+        q = dev(draw_shard(spec, seed, TENSOR_Q, spec.rank))
+        kb = [dev(draw_shard(spec, seed, TENSOR_K, j)) if j in sched else None for j in range(spec.N)]
+        vb = [dev(draw_shard(spec, seed, TENSOR_V, j)) if j in sched else None for j in range(spec.N)]
+        o = torch.empty((1, spec.L, spec.H, spec.d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((1, spec.H, spec.L), device="cuda")
+        ws = cp.alloc_workspace(desc)
+        ms = _timed(lambda: cp.cp_attn_rank_forward(desc, q, kb, vb, o, None, None, lse, workspace=ws,
+                                                    compute_stream=cs, copy_stream=xs,
+                                                    flags=cp.CP_RING_PREFETCH), cs, 2, reps)
+        fl = 4.0 * spec.d * spec.H * cp.cp_attn_visible_pairs(desc)
+        out[f"cfg{cfg}"] = {"workload": spec.name, "blocks": sched, "ms": round(ms, 4),
+                            "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+        del q, kb, vb, o, lse, ws
+    spec = cfgs[4]
+    desc = cp.Desc(spec.B, spec.H, spec.d, spec.N, spec.L, spec.rank, "bf16", spec.mask)
+    q = dev(draw_shard(spec, seed, TENSOR_Q, spec.rank))
+    kb = [dev(draw_shard(spec, seed, TENSOR_K, j)) for j in range(spec.N)]
+    vb = [dev(draw_shard(spec, seed, TENSOR_V, j)) for j in range(spec.N)]
+    big, vec = (1, spec.L, spec.H, spec.d), (1, spec.H, spec.L)
+    op = [torch.empty(big, device="cuda") for _ in range(spec.N)]
+    lp = [torch.empty(vec, device="cuda") for _ in range(spec.N)]
+    o = torch.empty(big, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(vec, device="cuda")
+    order = shuffled_order(seed, 4, spec.N)
+
+    def partials():
+        with torch.cuda.stream(cs):
+            for j in range(spec.N):
+                cp.cp_attn_block_partial(desc, j, cp.CP_MODE_PARTIAL_LSE, q, kb[j], vb[j], o_part=op[j],
+                                         lse_part=lp[j], stream=cs)
+
+    def merge():
+        cp.cp_attn_merge_lse(desc, op, lp, order, o, lse, stream=cs)
+
+    ms_p = _timed(partials, cs, 1, reps)
+    ms_m = _timed(merge, cs, 2, reps)
+    fl = 4.0 * spec.d * spec.H * cp.cp_attn_visible_pairs(desc)
+    rows = spec.L * spec.H
+    merge_bytes = spec.N * rows * (spec.d * 4 + 4) + rows * (spec.d * 2 + 4)
+    out["cfg4"] = {"workload": spec.name, "order": order, "partials_ms": round(ms_p, 4),
+                   "partials_tflops": round(fl / (ms_p * 1e-3) / 1e12, 2), "merge_ms": round(ms_m, 4),
+                   "merge_algorithmic_bytes": merge_bytes,
+                   "merge_gbs": round(merge_bytes / (ms_m * 1e-3) / 1e9, 1),
+                   "merge_frac_of_hbm": round(merge_bytes / (ms_m * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    return out
 
 
 def main():
@@ -234,6 +320,10 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
     prof.close()
+    del qd, kd, vd, out, m, lsum, lse, ws
+    if not args.no_secondary:
+        log("[bench] secondary workloads")
+        res["secondary"] = secondary(args.seed)
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows of head 0")
         res["cpu_baseline"] = cpu_baseline(spec, q, k, v, args.cpu_rows)
