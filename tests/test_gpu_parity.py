@@ -303,3 +303,84 @@ def test_full_size_partial_merge(cp):
     stats = check_o(o, ref["o"], "bf16")
     check_stat(host(lse)[:, heads][:, :, rows], ref["lse"], "bf16", "lse")
     say(f"[full cfg 4] order {order}: {stats}")
+
+
+# ----------------------------------------------------------------------------
+# API corners
+
+
+def test_merge_order_null_and_single_part(cp):
+    """merge_lse with order = NULL sums in index order (bit-identical to the
+    explicit identity order); with one part the output is that part."""
+    N, L, H, d = 3, 160, 2, 64
+    spec = ShardSpec(S=N * L, N=N, H=H, d=d, dtype="bf16", mask="none", cfg_id=107)
+    inp = make_inputs(spec, seed=8, ranks=[1])
+    desc = _desc(cp, spec, 1)
+    q = dev(inp["q"][1], "bf16")
+    big, vec = (1, L, H, d), (1, H, L)
+    ops, lps = [], []
+    for j in range(N):
+        op = torch.empty(big, device="cuda")
+        lp = torch.empty(vec, device="cuda")
+        cp.cp_attn_block_partial(desc, j, cp.CP_MODE_PARTIAL_LSE, q, dev(inp["k"][j], "bf16"),
+                                 dev(inp["v"][j], "bf16"), o_part=op, lse_part=lp)
+        ops.append(op)
+        lps.append(lp)
+    a, la = _outs(spec)[0], torch.empty(vec, device="cuda")
+    b, lb = _outs(spec)[0], torch.empty(vec, device="cuda")
+    cp.cp_attn_merge_lse(desc, ops, lps, None, a, la)
+    cp.cp_attn_merge_lse(desc, ops, lps, [0, 1, 2], b, lb)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    ref = oracle.rank_attention(inp["q"][1], inp["k"], inp["v"], 1, N, "none")
+    check_o(host(a), ref["o"], "bf16")
+    check_stat(host(la), ref["lse"], "bf16", "lse")
+    one, l1 = _outs(spec)[0], torch.empty(vec, device="cuda")
+    cp.cp_attn_merge_lse(desc, ops[1:2], lps[1:2], None, one, l1)
+    torch.cuda.synchronize()
+    # the weight exp(lse_0 - lse) is 1 up to the rounding of lse * log2(e): at most one bf16 ulp apart
+    assert torch.allclose(one.float(), ops[1], rtol=2.0 ** -8, atol=1e-6)
+    assert torch.allclose(l1, lps[1], rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_invisible_block_through_block_partial(cp, dtype):
+    """A block the rank never sees (causal, j > rank), called anyway: every
+    row is empty - PARTIAL_LSE gives O = 0 and lse = -inf, INIT gives
+    m = -inf, l = 0, O = 0."""
+    N, L, H, d = 4, 96, 2, 128
+    spec = ShardSpec(S=N * L, N=N, H=H, d=d, dtype=dtype, mask="causal", cfg_id=108)
+    inp = make_inputs(spec, seed=9, ranks=[1])
+    desc = _desc(cp, spec, 1)
+    q = dev(inp["q"][1], dtype)
+    k3, v3 = dev(inp["k"][3], dtype), dev(inp["v"][3], dtype)
+    big, vec = (1, L, H, d), (1, H, L)
+    op = torch.full(big, 7.0, device="cuda")
+    lp = torch.full(vec, 7.0, device="cuda")
+    cp.cp_attn_block_partial(desc, 3, cp.CP_MODE_PARTIAL_LSE, q, k3, v3, o_part=op, lse_part=lp)
+    st = (torch.full(big, 7.0, device="cuda"), torch.full(vec, 7.0, device="cuda"), torch.full(vec, 7.0, device="cuda"))
+    cp.cp_attn_block_partial(desc, 3, cp.CP_MODE_INIT, q, k3, v3, state=st)
+    torch.cuda.synchronize()
+    assert torch.all(op == 0) and torch.all(torch.isneginf(lp))
+    assert torch.all(st[0] == 0) and torch.all(torch.isneginf(st[1])) and torch.all(st[2] == 0)
+
+
+def test_profiler_records_each_attention_launch(cp):
+    spec = ShardSpec(S=4 * 384, N=4, H=2, d=128, dtype="bf16", mask="causal", cfg_id=109)
+    inp = make_inputs(spec, seed=10, ranks=[2])
+    kb, vb = _blocks(spec, inp)
+    desc = _desc(cp, spec, 2)
+    out, m, l, lse = _outs(spec)
+    ws = cp.alloc_workspace(desc)
+    prof = cp.Profiler(8)
+    cs, xs = torch.cuda.Stream(), torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    for _ in range(2):
+        cp.cp_attn_rank_forward(desc, dev(inp["q"][2], "bf16"), kb, vb, out, m, l, lse, workspace=ws,
+                                compute_stream=cs, copy_stream=xs, flags=cp.CP_RING_PREFETCH, profiler=prof)
+    cs.synchronize()
+    times = prof.read()
+    assert len(times) == 6 and all(t > 0 for t in times)      # rank 2 visits blocks 2, 1, 0 per call
+    prof.reset()
+    assert prof.read() == []
+    prof.close()
