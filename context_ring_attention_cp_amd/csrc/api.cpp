@@ -307,6 +307,12 @@ cp_status cp_attn_merge_lse(const cp_attn_desc* desc, int32_t n, const float* co
     a.o[t] = o_parts[j];
     a.lse[t] = lse_parts[j];
   }
+  // unused slots point at part 0, so no load the kernel guards by j < n can
+  // ever see a null address
+  for (int32_t t = n; t < kMaxParts; ++t) {
+    a.o[t] = a.o[0];
+    a.lse[t] = a.lse[0];
+  }
   a.n = n;
   a.L = desc->L;
   a.B = desc->B;

@@ -35,6 +35,12 @@ __device__ __forceinline__ void store4(void* out, int64_t off, bool bf, float4 v
   }
 }
 
+// Parts whose lse values are held in registers in one pass; longer merges
+// reread them.
+constexpr int kRegParts = 16;
+// Partials loaded back to back before their multiply-adds.
+constexpr int kBatch = 8;
+
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   const int d4 = a.d / 4;
   const int64_t total = (int64_t)a.B * a.L * a.H * d4;
@@ -47,26 +53,49 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   const int64_t row = br % a.L;
   const int b = (int)(br / a.L);
   const int64_t ml = ((int64_t)b * a.H + h) * a.L + row;
+  const int n = a.n;
 
   // lse = ln sum exp(lse_j), in base 2 with the max factored out
+  float l2[kRegParts];
   float mx = -INFINITY;
-  for (int j = 0; j < a.n; ++j) mx = fmaxf(mx, a.lse[j][ml]);
+#pragma unroll
+  for (int j = 0; j < kRegParts; ++j) {
+    l2[j] = j < n ? a.lse[j][ml] * kLog2e : -INFINITY;
+    mx = fmaxf(mx, l2[j]);
+  }
+  for (int j = kRegParts; j < n; ++j) mx = fmaxf(mx, a.lse[j][ml] * kLog2e);
   float4 o = float4{0.f, 0.f, 0.f, 0.f};
   float lse = -INFINITY;
   if (mx != -INFINITY) {
-    const float mx2 = mx * kLog2e;
     float tot = 0.f;
-    for (int j = 0; j < a.n; ++j) tot += __builtin_amdgcn_exp2f(__builtin_fmaf(a.lse[j][ml], kLog2e, -mx2));
-    const float lse2 = mx2 + __builtin_amdgcn_logf(tot);   // v_log_f32 is log2
+#pragma unroll
+    for (int j = 0; j < kRegParts; ++j) tot += __builtin_amdgcn_exp2f(l2[j] - mx);
+    for (int j = kRegParts; j < n; ++j) tot += __builtin_amdgcn_exp2f(__builtin_fmaf(a.lse[j][ml], kLog2e, -mx));
+    const float lse2 = mx + __builtin_amdgcn_logf(tot);   // v_log_f32 is log2
     lse = lse2 * kLn2;
     const int64_t off = rowhead * a.d + 4 * x4;
-    for (int j = 0; j < a.n; ++j) {
-      const float wj = __builtin_amdgcn_exp2f(__builtin_fmaf(a.lse[j][ml], kLog2e, -lse2));
-      const float4 v = *(const float4*)(a.o[j] + off);
-      o.x = __builtin_fmaf(wj, v.x, o.x);
-      o.y = __builtin_fmaf(wj, v.y, o.y);
-      o.z = __builtin_fmaf(wj, v.z, o.z);
-      o.w = __builtin_fmaf(wj, v.w, o.w);
+    // terms in the given order, kBatch partial loads in flight at a time
+    for (int j0 = 0; j0 < n; j0 += kBatch) {
+      float4 v[kBatch];
+      float wj[kBatch];
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) {
+        const int j = j0 + t;
+        v[t] = j < n ? *(const float4*)(a.o[j] + off) : float4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) {
+        const int j = j0 + t;
+        const float lj = j < kRegParts ? l2[j < kRegParts ? j : 0] : (j < n ? a.lse[j][ml] * kLog2e : -INFINITY);
+        wj[t] = j < n ? __builtin_amdgcn_exp2f(lj - lse2) : 0.f;
+      }
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) {
+        o.x = __builtin_fmaf(wj[t], v[t].x, o.x);
+        o.y = __builtin_fmaf(wj[t], v[t].y, o.y);
+        o.z = __builtin_fmaf(wj[t], v[t].z, o.z);
+        o.w = __builtin_fmaf(wj[t], v[t].w, o.w);
+      }
     }
   }
   store4(a.out, rowhead * a.d + 4 * x4, a.out_bf16, o);
