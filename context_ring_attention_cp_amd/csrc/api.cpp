@@ -60,6 +60,9 @@ cp_status check_desc(const cp_attn_desc* d) {
   if (S > 2147483647.0L) return fail(CP_ERR_UNSUPPORTED, "sequence N*L=%.0Lf exceeds int32 positions", S);
   const long double elems = (long double)d->B * d->L * d->H * d->d;
   if (elems * 4 > 4.0e18L) return fail(CP_ERR_UNSUPPORTED, "tensor of %.0Lf elements too large", elems);
+  // the bf16 kernel addresses the rows of one 64-key tile with 32-bit byte offsets
+  if ((long double)d->H * d->d * 4 * 64 > 4294967295.0L)
+    return fail(CP_ERR_UNSUPPORTED, "row stride H*d=%lld too large", (long long)d->H * d->d);
   // launch grid of the widest kernel (one workgroup per 64 rows of a head)
   const long double wgs = (long double)d->B * d->H * ((d->L + 63) / 64);
   if (wgs > 2147483647.0L) return fail(CP_ERR_UNSUPPORTED, "launch grid of %.0Lf workgroups too large", wgs);

@@ -146,7 +146,9 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  // wave index, uniform across the wave: everything derived from it (the
+  // wave's rows, its group, its tile thresholds) stays in scalar registers
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5;
   const int r32 = lane & 31;
   const int64_t L = a.L;
@@ -261,14 +263,18 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   const int f_ph = tid % CH;
   const uint32_t fk_off = (uint32_t)(((int64_t)f_row * rs + 8 * (f_ph ^ swz_k<D>(f_row))) * 2);
   const uint32_t fv_off = (uint32_t)(((int64_t)f_row * rs + 8 * (f_ph ^ swz_v<D>(f_row))) * 2);
-  auto fetch = [&](int kt, bf16* kd, bf16* vd) {
+  // LDS byte address of smem[st][tensor][e]: the stage, tensor and wave terms
+  // are uniform, so the fetch destinations are scalar arithmetic.
+  const uint32_t smem_base = lds_addr(&smem[0][0][0]);
+  auto lds_of = [&](int st, int tensor, int e) { return smem_base + (uint32_t)(((st * 2 + tensor) * TILE + e) * 2); };
+  auto fetch = [&](int kt, int st) {
     if ((int64_t)(kt + 1) * BN <= L) {
 #pragma unroll
       for (int i = 0; i < DMA; ++i) {
         const int64_t rowoff = ((int64_t)kt * BN + i * RPS) * rs;          // uniform
         const int wbase = (i * kFetchThreads + 64 * w) * 8;
-        fetch16(kg + rowoff, fk_off, lds_addr(kd + wbase));
-        fetch16(vg + rowoff, fv_off, lds_addr(vd + wbase));
+        fetch16(kg + rowoff, fk_off, lds_of(st, 0, wbase));
+        fetch16(vg + rowoff, fv_off, lds_of(st, 1, wbase));
       }
     } else {
 #pragma unroll
@@ -276,8 +282,8 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
         int64_t key = (int64_t)kt * BN + i * RPS + f_row;
         if (key > L - 1) key = L - 1;
         const int wbase = (i * kFetchThreads + 64 * w) * 8;
-        fetch16(kg, (uint32_t)((key * rs + 8 * (f_ph ^ swz_k<D>(f_row))) * 2), lds_addr(kd + wbase));
-        fetch16(vg, (uint32_t)((key * rs + 8 * (f_ph ^ swz_v<D>(f_row))) * 2), lds_addr(vd + wbase));
+        fetch16(kg, (uint32_t)((key * rs + 8 * (f_ph ^ swz_k<D>(f_row))) * 2), lds_of(st, 0, wbase));
+        fetch16(vg, (uint32_t)((key * rs + 8 * (f_ph ^ swz_v<D>(f_row))) * 2), lds_of(st, 1, wbase));
       }
     }
   };
@@ -318,13 +324,22 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
     }
   };
 
-  // Mask of tile kt: ragged tail, causal order, document boundaries.
-  auto need_mask = [&](int kt) -> bool {
-    const int64_t kbase = (int64_t)kt * BN;
-    const int64_t c_lo = a.k_pos0 + kbase;
-    const int64_t c_hi = a.k_pos0 + (kbase + BN < L ? kbase + BN : L) - 1;
-    return (kbase + BN > L) || (mask != MASK_NONE && (c_hi > pw_first || (doc && c_lo < ds_last)));
-  };
+  // Tiles of this wave that need a mask: the ragged last tile; with a causal
+  // mask the tiles from the first one holding a key after the wave's first
+  // query (key k_pos0 + kt BN + BN - 1 > pw_first); with documents also the
+  // tiles holding a key before the document start of the wave's last query
+  // (k_pos0 + kt BN < ds_last).  Thresholds in tiles, computed once.
+  const int ragged_kt = (L % BN != 0) ? nkt - 1 : -1;
+  int causal_from = nkt, doc_below = 0;
+  if (mask != MASK_NONE) {
+    const int64_t x = pw_first - a.k_pos0 - (BN - 1);       // tile needs it when kt BN > x
+    causal_from = x < 0 ? 0 : (int)(x / BN + 1 < nkt ? x / BN + 1 : nkt);
+    if (doc) {
+      const int64_t y = ds_last - a.k_pos0;                  // tile needs it when kt BN < y
+      doc_below = y <= 0 ? 0 : (int)((y + BN - 1) / BN < nkt ? (y + BN - 1) / BN : nkt);
+    }
+  }
+  auto need_mask = [&](int kt) -> bool { return kt == ragged_kt || kt >= causal_from || kt < doc_below; };
   auto apply_mask = [&](int kt, floatx16 (&sacc)[NT]) {
     // This lane's visible keys of the tile are the tile offsets [lo, hi]:
     // below the ragged end, not after its query (causal), not before its
@@ -426,8 +441,8 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
     const int grp = w >> 2;
     auto stage = [&](int u) { return (u - kt_begin) & (kStages - 1); };
     if (grp == 0) {
-      fetch(kt_begin, smem[0][0], smem[0][1]);
-      if (kt_begin + 1 < kt_end) fetch(kt_begin + 1, smem[1][0], smem[1][1]);
+      fetch(kt_begin, 0);
+      if (kt_begin + 1 < kt_end) fetch(kt_begin + 1, 1);
     }
     // every wave: the first two tiles (group 0) and the Q / state loads are done
     __builtin_amdgcn_s_waitcnt(0x0070);              // vmcnt(0) lgkmcnt(0)
@@ -443,8 +458,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
       // softmax phase; group 0 first starts the fetch of tile u+2
       const bool more = u + 2 < kt_end;
       if (grp == 0 && more) {
-        const int sf = stage(u + 2);
-        fetch(u + 2, smem[sf][0], smem[sf][1]);
+        fetch(u + 2, stage(u + 2));
       }
       if (u < kt_end) {
         if (need_mask(u)) apply_mask(u, sacc);
