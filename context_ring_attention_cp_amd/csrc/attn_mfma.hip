@@ -259,8 +259,13 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   constexpr int RPS = kFetchThreads / CH;        // rows covered by one fetch of the 256 lanes
   static_assert(DMA >= 1 && (BN * CH) % kFetchThreads == 0, "tile fetch split");
   static_assert((D == 128 && RPS % 16 == 0) || (D == 64 && RPS % 16 == 0), "swizzle bits below RPS");
-  const int f_row = tid / CH;
-  const int f_ph = tid % CH;
+  // lane index within the fetching group of kFetchThreads threads (and its
+  // wave within the group): the slot of a fetch never depends on which group
+  // issues it
+  const int f_tid = tid & (kFetchThreads - 1);
+  const int f_w = w & (kFetchThreads / 64 - 1);
+  const int f_row = f_tid / CH;
+  const int f_ph = f_tid % CH;
   const uint32_t fk_off = (uint32_t)(((int64_t)f_row * rs + 8 * (f_ph ^ swz_k<D>(f_row))) * 2);
   const uint32_t fv_off = (uint32_t)(((int64_t)f_row * rs + 8 * (f_ph ^ swz_v<D>(f_row))) * 2);
   // LDS byte address of smem[st][tensor][e]: the stage, tensor and wave terms
@@ -272,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
 #pragma unroll
       for (int i = 0; i < DMA; ++i) {
         const int64_t rowoff = ((int64_t)kt * BN + i * RPS) * rs;          // uniform
-        const int wbase = (i * kFetchThreads + 64 * w) * 8;
+        const int wbase = (i * kFetchThreads + 64 * f_w) * 8;
         fetch16(kg + rowoff, fk_off, lds_of(st, 0, wbase));
         fetch16(vg + rowoff, fv_off, lds_of(st, 1, wbase));
       }
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
       for (int i = 0; i < DMA; ++i) {
         int64_t key = (int64_t)kt * BN + i * RPS + f_row;
         if (key > L - 1) key = L - 1;
-        const int wbase = (i * kFetchThreads + 64 * w) * 8;
+        const int wbase = (i * kFetchThreads + 64 * f_w) * 8;
         fetch16(kg, (uint32_t)((key * rs + 8 * (f_ph ^ swz_k<D>(f_row))) * 2), lds_of(st, 0, wbase));
         fetch16(vg, (uint32_t)((key * rs + 8 * (f_ph ^ swz_v<D>(f_row))) * 2), lds_of(st, 1, wbase));
       }
