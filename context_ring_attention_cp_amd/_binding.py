@@ -32,6 +32,7 @@ EXPORTED = [
     "cp_attn_rank_forward", "cp_attn_ring_schedule", "cp_attn_visible_pairs",
     "cp_attn_profiler_create", "cp_attn_profiler_reset", "cp_attn_profiler_read",
     "cp_attn_profiler_destroy", "cp_attn_status_string", "cp_attn_last_error",
+    "cp_attn_bwd_delta", "cp_attn_block_backward", "cp_attn_rank_backward",
 ]
 
 
@@ -83,6 +84,10 @@ def lib() -> ctypes.CDLL:
         L.cp_attn_profiler_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)]
         L.cp_attn_profiler_destroy.argtypes = [vp]
         L.cp_attn_profiler_destroy.restype = None
+        L.cp_attn_bwd_delta.argtypes = [dp, vp, vp, f32p, vp]
+        L.cp_attn_block_backward.argtypes = [dp, i32, i32, vp, vp, vp, vp, f32p, f32p, f32p, f32p, f32p, vp]
+        L.cp_attn_rank_backward.argtypes = [dp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, f32p, f32p,
+                                            f32p, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp]
         L.cp_attn_status_string.argtypes = [i32]
         L.cp_attn_status_string.restype = ctypes.c_char_p
         L.cp_attn_last_error.argtypes = []
@@ -265,6 +270,54 @@ def cp_attn_rank_forward(desc: Desc, q, k_blocks: Sequence, v_blocks: Sequence, 
                                       _ptr(lse_out), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), cs, xs, int(flags),
                                       profiler.handle if profiler is not None else None))
+
+
+def cp_attn_bwd_delta(desc: Desc, o, d_o, delta, stream=None) -> None:
+    import torch
+    big, vec = _shapes(desc)
+    _check_tensor(o, "o", big, torch.bfloat16)
+    _check_tensor(d_o, "d_o", big, torch.bfloat16)
+    _check_tensor(delta, "delta", vec, torch.float32)
+    _check(lib().cp_attn_bwd_delta(desc.ref, _ptr(o), _ptr(d_o), _ptr(delta), _stream(stream)))
+
+
+def cp_attn_block_backward(desc: Desc, j: int, mode: int, q, k_j, v_j, d_o, lse, delta, dq, dk_j, dv_j,
+                           stream=None) -> None:
+    import torch
+    big, vec = _shapes(desc)
+    for n, t in (("q", q), ("k_j", k_j), ("v_j", v_j), ("d_o", d_o)):
+        _check_tensor(t, n, big, torch.bfloat16)
+    for n, t in (("lse", lse), ("delta", delta)):
+        _check_tensor(t, n, vec, torch.float32)
+    for n, t in (("dq", dq), ("dk_j", dk_j), ("dv_j", dv_j)):
+        _check_tensor(t, n, big, torch.float32)
+    _check(lib().cp_attn_block_backward(desc.ref, int(j), int(mode), _ptr(q), _ptr(k_j), _ptr(v_j), _ptr(d_o),
+                                        _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk_j), _ptr(dv_j),
+                                        _stream(stream)))
+
+
+def cp_attn_rank_backward(desc: Desc, q, k_blocks: Sequence, v_blocks: Sequence, o, d_o, lse, delta, dq,
+                          dk_blocks: Sequence, dv_blocks: Sequence, flags: int = 0, stream=None) -> None:
+    import torch
+    big, vec = _shapes(desc)
+    N = desc.c.N
+    if not (len(k_blocks) == len(v_blocks) == len(dk_blocks) == len(dv_blocks) == N):
+        raise ValueError(f"need N={N} entries in k_blocks, v_blocks, dk_blocks and dv_blocks")
+    for n, t in (("q", q), ("o", o), ("d_o", d_o)):
+        _check_tensor(t, n, big, torch.bfloat16)
+    for t in list(k_blocks) + list(v_blocks):
+        _check_tensor(t, "k/v block", big, torch.bfloat16)
+    for n, t in (("lse", lse), ("delta", delta)):
+        _check_tensor(t, n, vec, torch.float32)
+    _check_tensor(dq, "dq", big, torch.float32)
+    for t in list(dk_blocks) + list(dv_blocks):
+        _check_tensor(t, "dk/dv block", big, torch.float32)
+    kp = (ctypes.c_void_p * N)(*[_ptr(t) for t in k_blocks])
+    vp = (ctypes.c_void_p * N)(*[_ptr(t) for t in v_blocks])
+    dkp = (ctypes.c_void_p * N)(*[_ptr(t) for t in dk_blocks])
+    dvp = (ctypes.c_void_p * N)(*[_ptr(t) for t in dv_blocks])
+    _check(lib().cp_attn_rank_backward(desc.ref, _ptr(q), kp, vp, _ptr(o), _ptr(d_o), _ptr(lse), _ptr(delta),
+                                       _ptr(dq), dkp, dvp, int(flags), _stream(stream)))
 
 
 def cp_attn_ring_schedule(desc: Desc, flags: int = 0):

@@ -358,6 +358,148 @@ cp_status cp_attn_finalize(const cp_attn_desc* desc, const cp_state* state, void
   return CP_OK;
 }
 
+namespace {
+
+cp_status check_bwd_desc(const cp_attn_desc* d) {
+  const cp_status st = check_desc(d);
+  if (st != CP_OK) return st;
+  if (d->dtype != CP_BF16) return fail(CP_ERR_UNSUPPORTED, "the backward takes bf16 inputs (dtype=%d)", d->dtype);
+  return CP_OK;
+}
+
+int64_t tensor_elems(const cp_attn_desc* d) { return (int64_t)d->B * d->L * d->H * d->d; }
+
+BwdArgs bwd_args(const cp_attn_desc* d, int32_t j, const void* q, const void* k, const void* v, const void* d_o,
+                 const float* lse, const float* delta, float* dq, float* dk, float* dv, bool accumulate) {
+  BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.d_o = d_o;
+  a.lse = lse;
+  a.delta = delta;
+  a.L = d->L;
+  a.B = d->B;
+  a.H = d->H;
+  a.q_pos0 = (int64_t)d->rank * d->L;
+  a.k_pos0 = (int64_t)j * d->L;
+  a.mask = d->mask;
+  a.ndocs = d->ndocs;
+  a.cu = d->mask == CP_MASK_DOC_CAUSAL ? d->cu_seqlens_dev : nullptr;
+  a.scale_log2 = scale_log2(d);
+  a.scale = a.scale_log2 / 1.442695040888963407360f;
+  a.accumulate = accumulate ? 1 : 0;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  return a;
+}
+
+// One block's backward after validation: kernels for a visible block, zeros
+// for an invisible one (dq only with INIT).
+cp_status run_block_backward(const cp_attn_desc* d, int32_t j, bool accumulate, const void* q, const void* k,
+                             const void* v, const void* d_o, const float* lse, const float* delta, float* dq,
+                             float* dk, float* dv, hipStream_t s) {
+  hipError_t e;
+  if (!block_visible(d, j)) {
+    const int64_t n = tensor_elems(d);
+    if ((e = launch_zero(dk, n, s)) != hipSuccess) return hip_fail(e, "zero fill");
+    if ((e = launch_zero(dv, n, s)) != hipSuccess) return hip_fail(e, "zero fill");
+    if (!accumulate && (e = launch_zero(dq, n, s)) != hipSuccess) return hip_fail(e, "zero fill");
+    return CP_OK;
+  }
+  const BwdArgs a = bwd_args(d, j, q, k, v, d_o, lse, delta, dq, dk, dv, accumulate);
+  if ((e = launch_bwd_blocks(a, d->d, s)) != hipSuccess) return hip_fail(e, "backward kernel launch");
+  return CP_OK;
+}
+
+}  // namespace
+
+cp_status cp_attn_bwd_delta(const cp_attn_desc* desc, const void* o, const void* d_o, float* delta, void* stream) {
+  g_last_error.clear();
+  cp_status st = check_bwd_desc(desc);
+  if (st != CP_OK) return st;
+  if ((st = check_tensor(o, "o")) != CP_OK || (st = check_tensor(d_o, "d_o")) != CP_OK ||
+      (st = check_vec(delta, "delta", false)) != CP_OK)
+    return st;
+  DeltaArgs a;
+  a.o = o;
+  a.d_o = d_o;
+  a.L = desc->L;
+  a.B = desc->B;
+  a.H = desc->H;
+  a.delta = delta;
+  const hipError_t e = launch_bwd_delta(a, desc->d, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "delta kernel launch");
+  return CP_OK;
+}
+
+cp_status cp_attn_block_backward(const cp_attn_desc* desc, int32_t j, int32_t mode, const void* q, const void* k_j,
+                                 const void* v_j, const void* d_o, const float* lse, const float* delta, float* dq,
+                                 float* dk_j, float* dv_j, void* stream) {
+  g_last_error.clear();
+  cp_status st = check_bwd_desc(desc);
+  if (st != CP_OK) return st;
+  if (j < 0 || j >= desc->N) return fail(CP_ERR_INVALID_ARG, "block j=%d outside [0, N=%d)", j, desc->N);
+  if (mode != CP_MODE_INIT && mode != CP_MODE_ACCUMULATE)
+    return fail(CP_ERR_INVALID_ARG, "mode=%d: the backward takes INIT or ACCUMULATE", mode);
+  if ((st = check_tensor(q, "q")) != CP_OK || (st = check_tensor(k_j, "k_j")) != CP_OK ||
+      (st = check_tensor(v_j, "v_j")) != CP_OK || (st = check_tensor(d_o, "d_o")) != CP_OK ||
+      (st = check_vec(lse, "lse", false)) != CP_OK || (st = check_vec(delta, "delta", false)) != CP_OK ||
+      (st = check_tensor(dq, "dq")) != CP_OK || (st = check_tensor(dk_j, "dk_j")) != CP_OK ||
+      (st = check_tensor(dv_j, "dv_j")) != CP_OK)
+    return st;
+  return run_block_backward(desc, j, mode == CP_MODE_ACCUMULATE, q, k_j, v_j, d_o, lse, delta, dq, dk_j, dv_j,
+                            (hipStream_t)stream);
+}
+
+cp_status cp_attn_rank_backward(const cp_attn_desc* desc, const void* q, const void* const* k_blocks,
+                                const void* const* v_blocks, const void* o, const void* d_o, const float* lse,
+                                float* delta, float* dq, float* const* dk_blocks, float* const* dv_blocks,
+                                int32_t flags, void* stream) {
+  g_last_error.clear();
+  cp_status st = check_bwd_desc(desc);
+  if (st != CP_OK) return st;
+  if (flags & ~CP_RING_REVERSE) return fail(CP_ERR_INVALID_ARG, "unknown flags 0x%x (only CP_RING_REVERSE)", flags);
+  if ((st = check_tensor(q, "q")) != CP_OK || (st = check_tensor(o, "o")) != CP_OK ||
+      (st = check_tensor(d_o, "d_o")) != CP_OK || (st = check_vec(lse, "lse", false)) != CP_OK ||
+      (st = check_vec(delta, "delta", false)) != CP_OK || (st = check_tensor(dq, "dq")) != CP_OK)
+    return st;
+  if (!k_blocks || !v_blocks || !dk_blocks || !dv_blocks)
+    return fail(CP_ERR_INVALID_ARG, "k_blocks/v_blocks/dk_blocks/dv_blocks is NULL");
+  const std::vector<int32_t> sched = schedule(desc, flags);
+  for (int32_t j = 0; j < desc->N; ++j) {
+    if ((st = check_tensor(dk_blocks[j], "dk_blocks[j]")) != CP_OK ||
+        (st = check_tensor(dv_blocks[j], "dv_blocks[j]")) != CP_OK)
+      return st;
+  }
+  for (int32_t j : sched) {
+    if ((st = check_tensor(k_blocks[j], "k_blocks[j]")) != CP_OK || (st = check_tensor(v_blocks[j], "v_blocks[j]")) != CP_OK)
+      return st;
+  }
+  if (sched.empty()) return fail(CP_ERR_INVALID_ARG, "no visible block");   // unreachable: the diagonal is visible
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = cp_attn_bwd_delta(desc, o, d_o, delta, stream)) != CP_OK) return st;
+  std::vector<char> seen(desc->N, 0);
+  bool first = true;
+  for (int32_t j : sched) {
+    if ((st = run_block_backward(desc, j, !first, q, k_blocks[j], v_blocks[j], d_o, lse, delta, dq, dk_blocks[j],
+                                 dv_blocks[j], s)) != CP_OK)
+      return st;
+    seen[j] = 1;
+    first = false;
+  }
+  const int64_t n = tensor_elems(desc);
+  for (int32_t j = 0; j < desc->N; ++j) {
+    if (seen[j]) continue;
+    hipError_t e;
+    if ((e = launch_zero(dk_blocks[j], n, s)) != hipSuccess || (e = launch_zero(dv_blocks[j], n, s)) != hipSuccess)
+      return hip_fail(e, "zero fill");
+  }
+  return CP_OK;
+}
+
 cp_status cp_attn_rank_forward(const cp_attn_desc* desc, const void* q, const void* const* k_blocks,
                                const void* const* v_blocks, void* out, float* m_out, float* l_out, float* lse_out,
                                void* workspace, size_t workspace_bytes, void* compute_stream, void* copy_stream,

@@ -71,10 +71,43 @@ struct FinalizeArgs {
   float* lse_out;
 };
 
+// Backward of one block (bf16 inputs, fp32 gradients).
+struct BwdArgs {
+  const void* q;         // [B, L, H, d] the rank's queries
+  const void* k;         // [B, L, H, d] block j
+  const void* v;         // [B, L, H, d] block j
+  const void* d_o;       // [B, L, H, d] gradient of the rank's output
+  const float* lse;      // [B, H, L] log-sum-exp of the rank's forward (natural log)
+  const float* delta;    // [B, H, L] rowsum(dO * O)
+  int64_t L;
+  int32_t B, H;
+  int64_t q_pos0, k_pos0;
+  int32_t mask;
+  int32_t ndocs;
+  const int32_t* cu;     // device cu_seqlens (DOC_CAUSAL)
+  float scale;           // softmax scale
+  float scale_log2;      // scale * log2(e)
+  int32_t accumulate;    // dq += (1) or dq = (0)
+  float* dq;             // [B, L, H, d]
+  float* dk;             // [B, L, H, d] of block j
+  float* dv;             // [B, L, H, d] of block j
+};
+
+struct DeltaArgs {
+  const void* o;         // [B, L, H, d] bf16
+  const void* d_o;       // [B, L, H, d] bf16
+  int64_t L;
+  int32_t B, H;
+  float* delta;          // [B, H, L]
+};
+
 // Launchers return the hipError_t of the launch.
 hipError_t launch_block_bf16(const BlockArgs& a, int d, hipStream_t s);
 hipError_t launch_block_f32(const BlockArgs& a, int d, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
+hipError_t launch_bwd_delta(const DeltaArgs& a, int d, hipStream_t s);
+hipError_t launch_bwd_blocks(const BwdArgs& a, int d, hipStream_t s);   // dq kernel, then dk/dv kernel
+hipError_t launch_zero(float* p, int64_t n, hipStream_t s);            // n a multiple of 4
 
 }  // namespace cpattn

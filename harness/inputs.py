@@ -21,7 +21,7 @@ from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_DOCS = 0, 1, 2, 3
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_DOCS, TENSOR_DO = 0, 1, 2, 3, 4
 
 MASK_NONE, MASK_CAUSAL, MASK_DOC_CAUSAL = "none", "causal", "doc_causal"
 MASKS = (MASK_NONE, MASK_CAUSAL, MASK_DOC_CAUSAL)
@@ -112,6 +112,15 @@ def draw_shard(spec: ShardSpec, seed: int, tensor_id: int, block: int) -> np.nda
     x = normal_block(seed, spec.cfg_id, tensor_id, block, spec.shard_shape())
     if tensor_id == TENSOR_Q and spec.q_scale != 1.0:
         x = x * np.float32(spec.q_scale)
+    if spec.dtype == "bf16":
+        x = round_to_bf16(x)
+    return x
+
+
+def draw_grad(spec: ShardSpec, seed: int, rank: int) -> np.ndarray:
+    """Upstream gradient dO of rank ``rank``'s output, N(0, 1), float32,
+    rounded to bf16 when spec.dtype == 'bf16' (the backward's input)."""
+    x = normal_block(seed, spec.cfg_id, TENSOR_DO, rank, spec.shard_shape())
     if spec.dtype == "bf16":
         x = round_to_bf16(x)
     return x

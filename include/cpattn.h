@@ -181,6 +181,60 @@ cp_status cp_attn_rank_forward(const cp_attn_desc* desc, const void* q,
                                void* workspace, size_t workspace_bytes, void* compute_stream,
                                void* copy_stream, int32_t flags, cp_attn_profiler* prof);
 
+/* ---- Backward of one rank shard ------------------------------------------
+ * The backward walks the ring's K/V blocks again and recomputes what the
+ * forward did not keep (compassingai.com page, section "反向傳播"; the Q, K, V
+ * gradients go back around the ring, process-cxr.github.io page, section
+ * "Long Context Attention 中的通信").  Per visible block j, with P_j
+ * recomputed from the forward's log-sum-exp and the chain rule of the forward
+ * definition (compassingai.com page, section "數學基礎"):
+ *   P_j = exp(Q K_j^T * scale - lse) (masked),  dP_j = dO V_j^T,
+ *   dS_j = P_j * (dP_j - delta),  delta = rowsum(dO * O),
+ *   dQ += scale dS_j K_j,  dK_j = scale dS_j^T Q,  dV_j = P_j^T dO.
+ * dK_j, dV_j are this rank's contributions to block j's gradients; summed over
+ * all ranks they give the full-sequence gradient.  bf16 inputs only (an f32
+ * desc gives CP_ERR_UNSUPPORTED); gradients are float32.  The scale is the
+ * desc's (1/sqrt(d) when 0), the same as the forward's. */
+
+/* delta [B, H, L] (device float32) = sum over the head dim of dO * O, with
+ * o the forward output and d_o its gradient (device bf16 [B, L, H, d]).
+ * Errors: CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED, CP_ERR_HIP. */
+cp_status cp_attn_bwd_delta(const cp_attn_desc* desc, const void* o, const void* d_o, float* delta,
+                            void* stream);
+
+/* One block's backward for block j (0 <= j < N) of the desc's ring.
+ *   q, k_j, v_j, d_o : device bf16 [B, L, H, d];
+ *   lse              : device [B, H, L] float32, the forward's lse over ALL
+ *                      blocks (natural log, e.g. lse_out of
+ *                      cp_attn_rank_forward);
+ *   delta            : device [B, H, L] float32 from cp_attn_bwd_delta;
+ *   dq               : device [B, L, H, d] float32: mode CP_MODE_INIT writes
+ *                      this block's dQ part, CP_MODE_ACCUMULATE adds it;
+ *   dk_j, dv_j       : device [B, L, H, d] float32, written (zero when no row
+ *                      of the rank sees the block).
+ * Rows whose lse is -inf contribute nothing.
+ * Errors: CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED, CP_ERR_HIP. */
+cp_status cp_attn_block_backward(const cp_attn_desc* desc, int32_t j, int32_t mode, const void* q,
+                                 const void* k_j, const void* v_j, const void* d_o, const float* lse,
+                                 const float* delta, float* dq, float* dk_j, float* dv_j, void* stream);
+
+/* The whole backward of rank desc->rank: delta, then every block in the
+ * forward's ring order (CP_RING_REVERSE honoured), all on `stream`.
+ *   k_blocks, v_blocks : HOST arrays of N device bf16 pointers (as for the
+ *                        forward; only visible blocks are read);
+ *   o, d_o             : device bf16 [B, L, H, d]: forward output, its gradient;
+ *   lse                : device [B, H, L] float32 of the forward;
+ *   delta              : device [B, H, L] float32, written (caller-owned scratch);
+ *   dq                 : device [B, L, H, d] float32, written;
+ *   dk_blocks, dv_blocks : HOST arrays of N device float32 [B, L, H, d]
+ *                        pointers, each written (zeros for blocks the rank
+ *                        does not see).
+ * Errors: CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED, CP_ERR_HIP. */
+cp_status cp_attn_rank_backward(const cp_attn_desc* desc, const void* q, const void* const* k_blocks,
+                                const void* const* v_blocks, const void* o, const void* d_o,
+                                const float* lse, float* delta, float* dq, float* const* dk_blocks,
+                                float* const* dv_blocks, int32_t flags, void* stream);
+
 /* Host-only: the blocks cp_attn_rank_forward computes on, in visiting order.
  * Writes at most `capacity` block ids to blocks_out and the count to
  * *count_out.  Errors: CP_ERR_INVALID_ARG (also when capacity is too small). */

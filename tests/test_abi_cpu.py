@@ -266,3 +266,50 @@ def test_status_strings():
     assert B.status_string(99) == "CP_ERR_UNKNOWN"
     assert B.cp_attn_visible_pairs(_desc()) > 0
     assert B.last_error() == ""
+
+
+def test_backward_argument_errors():
+    d = _desc()
+    lib = B.lib()
+    F = FAKE
+    P = ctypes.c_void_p
+    blk = (P * 4)(F, F + 256, F + 512, F + 768)
+    bad = (P * 4)(F, F + 256, None, F + 768)
+    cases_block = [
+        ((d.ref, 4, B.CP_MODE_INIT, F, F, F, F, F, F, F, F, F, None), B.CP_ERR_INVALID_ARG, "block j"),
+        ((d.ref, 0, B.CP_MODE_PARTIAL_LSE, F, F, F, F, F, F, F, F, F, None), B.CP_ERR_INVALID_ARG, "INIT or ACCUMULATE"),
+        ((d.ref, 0, B.CP_MODE_INIT, None, F, F, F, F, F, F, F, F, None), B.CP_ERR_INVALID_ARG, "q is NULL"),
+        ((d.ref, 0, B.CP_MODE_INIT, F, F, F, F + 8, F, F, F, F, F, None), B.CP_ERR_INVALID_ARG, "d_o is not 16-byte"),
+        ((d.ref, 0, B.CP_MODE_INIT, F, F, F, F, None, F, F, F, F, None), B.CP_ERR_INVALID_ARG, "lse is NULL"),
+        ((d.ref, 0, B.CP_MODE_INIT, F, F, F, F, F, F + 2, F, F, F, None), B.CP_ERR_INVALID_ARG, "delta"),
+        ((d.ref, 0, B.CP_MODE_INIT, F, F, F, F, F, F, F + 4, F, F, None), B.CP_ERR_INVALID_ARG, "dq"),
+        ((d.ref, 0, B.CP_MODE_INIT, F, F, F, F, F, F, F, None, F, None), B.CP_ERR_INVALID_ARG, "dk_j"),
+        ((d.ref, 0, B.CP_MODE_INIT, F, F, F, F, F, F, F, F, None, None), B.CP_ERR_INVALID_ARG, "dv_j"),
+    ]
+    for args, status, msg in cases_block:
+        assert _status(lib.cp_attn_block_backward, *args) == status, (args, B.last_error())
+        assert msg in B.last_error(), (msg, B.last_error())
+    # f32 descs are refused by every backward entry point
+    f = _desc(dtype="f32")
+    assert _status(lib.cp_attn_bwd_delta, f.ref, F, F, F, None) == B.CP_ERR_UNSUPPORTED
+    assert "bf16" in B.last_error()
+    assert _status(lib.cp_attn_block_backward, f.ref, 0, B.CP_MODE_INIT, F, F, F, F, F, F, F, F, F,
+                   None) == B.CP_ERR_UNSUPPORTED
+    assert _status(lib.cp_attn_rank_backward, f.ref, F, blk, blk, F, F, F, F, F, blk, blk, 0,
+                   None) == B.CP_ERR_UNSUPPORTED
+    # delta
+    assert _status(lib.cp_attn_bwd_delta, d.ref, None, F, F, None) == B.CP_ERR_INVALID_ARG
+    assert _status(lib.cp_attn_bwd_delta, d.ref, F, F, F + 1, None) == B.CP_ERR_INVALID_ARG
+    # rank driver
+    cases_rank = [
+        ((d.ref, F, blk, blk, F, F, F, F, F, blk, blk, B.CP_RING_PREFETCH, None), "flags"),
+        ((d.ref, F, None, blk, F, F, F, F, F, blk, blk, 0, None), "NULL"),
+        ((d.ref, F, blk, blk, F, F, F, F, F, bad, blk, 0, None), "dk_blocks[j]"),
+        ((d.ref, F, blk, blk, F, F, F, F, F, blk, bad, 0, None), "dv_blocks[j]"),
+        ((d.ref, F, bad, blk, F, F, F, F, F, blk, blk, 0, None), "k_blocks[j]"),
+        ((d.ref, F, blk, blk, None, F, F, F, F, blk, blk, 0, None), "o is NULL"),
+        ((d.ref, F, blk, blk, F, F, F, None, F, blk, blk, 0, None), "delta"),
+    ]
+    for args, msg in cases_rank:
+        assert _status(lib.cp_attn_rank_backward, *args) == B.CP_ERR_INVALID_ARG, (msg, B.last_error())
+        assert msg in B.last_error(), (msg, B.last_error())
