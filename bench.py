@@ -29,15 +29,20 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk (the published 2.5 PF)
 PEAK_HBM_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "context_ring_attention_cp_amd", "csrc", "attn_mfma.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "context_ring_attention_cp_amd", "csrc", f)
+               for f in ("attn_mfma.hip", "gfx950_util.h", "kernels.h")]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "attn_block_bf16__causal_128k_last_rank.traffic.json")
 ATTN_KERNEL = "attn_block_bf16_kernel<128>"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
 def kernel_sha256() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 over the sources the forward block kernel is compiled from."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _pmc_rows(d: str, counter: str):
@@ -219,6 +224,36 @@ def secondary(seed: int, reps: int = 5):
     return out
 
 
+def backward(spec, seed, desc, qd, kd, vd, out, lse, pairs, stream, reps: int = 3) -> dict:
+    """cp_attn_rank_backward of the benchmarked shard (delta, then the dQ and
+    dK/dV kernels per visible block), with the forward's out and lse and a
+    seeded dO.  tflops counts the algorithmic 10 d flops per visible pair (the
+    five products S, dP, dV, dK, dQ); the kernels execute 14 d (S and dP are
+    computed by both kernels), reported as mfma_tflops."""
+    import torch
+
+    import context_ring_attention_cp_amd as cp
+    from harness.inputs import bf16_bits, draw_grad
+
+    big, vec = (spec.B, spec.L, spec.H, spec.d), (spec.B, spec.H, spec.L)
+    do = torch.from_numpy(np.ascontiguousarray(bf16_bits(draw_grad(spec, seed, spec.rank))).view(np.int16))
+    do = do.view(torch.bfloat16).to("cuda")
+    delta = torch.empty(vec, device="cuda")
+    dq = torch.empty(big, device="cuda")
+    dk = [torch.empty(big, device="cuda") for _ in range(spec.N)]
+    dv = [torch.empty(big, device="cuda") for _ in range(spec.N)]
+    ms = _timed(lambda: cp.cp_attn_rank_backward(desc, qd, kd, vd, out, do, lse, delta, dq, dk, dv, stream=stream),
+                stream, 1, reps)
+    assert torch.isfinite(dq).all(), "non-finite dq"
+    fl = 10.0 * spec.d * spec.B * spec.H * pairs
+    res = {"workload": "backward of the benchmarked shard (rank_backward: delta, dQ and dK/dV kernels per block)",
+           "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+           "pct_of_peak": round(100.0 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+           "mfma_tflops": round(1.4 * fl / (ms * 1e-3) / 1e12, 2), "flops_counted": fl}
+    del do, delta, dq, dk, dv
+    return res
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -320,7 +355,11 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
     prof.close()
-    del qd, kd, vd, out, m, lsum, lse, ws
+    del m, lsum, ws
+    if not args.no_secondary:
+        log("[bench] backward of the same shard")
+        res["backward"] = backward(spec, args.seed, desc, qd, kd, vd, out, lse, pairs, cs)
+    del qd, kd, vd, out, lse
     if not args.no_secondary:
         log("[bench] secondary workloads")
         res["secondary"] = secondary(args.seed)
