@@ -158,8 +158,9 @@ def _timed(fn, stream, warmup: int, reps: int) -> float:
 def secondary(seed: int, reps: int = 5):
     """The other workloads of the path, timed briefly: the causal 32K
     last-rank shard, the packed-document shard (rank_forward, ring prefetch),
-    and the bidirectional 64K merge stress case (8 PARTIAL_LSE launches, then
-    one merge in a shuffled order; the merge is reported against HBM)."""
+    the bidirectional 64K merge stress case (8 PARTIAL_LSE launches, then one
+    merge in a shuffled order; the merge is reported against HBM), and one
+    rank's share of all-to-all (Ulysses) context parallelism at 128K."""
     import torch
 
     import context_ring_attention_cp_amd as cp
@@ -221,6 +222,29 @@ def secondary(seed: int, reps: int = 5):
                    "merge_algorithmic_bytes": merge_bytes,
                    "merge_gbs": round(merge_bytes / (ms_m * 1e-3) / 1e9, 1),
                    "merge_frac_of_hbm": round(merge_bytes / (ms_m * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del q, kb, vb, op, lp, o, lse
+    # All-to-all (Ulysses) share of the 128K example: rank 3 of 4 runs the
+    # whole sequence (S = 131072) on its 8 of 32 heads; the two all-to-alls are
+    # the regrouping copies.  Seeded N(0, 1) inputs drawn on the device.
+    spec = cfgs[3]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed + 303)
+    shape = (spec.B, spec.L, spec.H, spec.d)
+    qs, ks, vs = ([torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16) for _ in range(spec.N)]
+                  for _ in range(3))
+    os_ = [torch.empty(shape, dtype=torch.bfloat16, device="cuda") for _ in range(spec.N)]
+    desc = cp.Desc(spec.B, spec.H, spec.d, spec.N, spec.L, spec.rank, "bf16", "causal")
+    ws = cp.alloc_ulysses_workspace(desc)
+    hn = spec.H // spec.N
+    lse = torch.empty((spec.B, hn, spec.S), device="cuda")
+    ms = _timed(lambda: cp.cp_attn_ulysses_forward(desc, qs, ks, vs, os_, None, None, lse, workspace=ws, stream=cs),
+                cs, 2, reps)
+    fl = 4.0 * spec.d * hn * spec.B * spec.S * (spec.S + 1) / 2
+    regroup = 8 * spec.B * spec.S * hn * spec.d * 2      # Q, K, V gathered and O scattered, each read + written
+    out["ulysses"] = {"workload": "all-to-all (Ulysses) share of the 128K example: rank 3 of 4, 8 of 32 heads "
+                                  "over S=131072, causal, bf16; the two all-to-alls simulated by regrouping copies",
+                      "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "regroup_bytes": regroup}
+    del qs, ks, vs, os_, ws, lse
     return out
 
 

@@ -33,6 +33,7 @@ EXPORTED = [
     "cp_attn_profiler_create", "cp_attn_profiler_reset", "cp_attn_profiler_read",
     "cp_attn_profiler_destroy", "cp_attn_status_string", "cp_attn_last_error",
     "cp_attn_bwd_delta", "cp_attn_block_backward", "cp_attn_rank_backward",
+    "cp_attn_ulysses_workspace_bytes", "cp_attn_ulysses_forward",
 ]
 
 
@@ -88,6 +89,10 @@ def lib() -> ctypes.CDLL:
         L.cp_attn_block_backward.argtypes = [dp, i32, i32, vp, vp, vp, vp, f32p, f32p, f32p, f32p, f32p, vp]
         L.cp_attn_rank_backward.argtypes = [dp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, f32p, f32p,
                                             f32p, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp]
+        L.cp_attn_ulysses_workspace_bytes.argtypes = [dp]
+        L.cp_attn_ulysses_workspace_bytes.restype = ctypes.c_size_t
+        L.cp_attn_ulysses_forward.argtypes = [dp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                              ctypes.POINTER(vp), f32p, f32p, f32p, vp, ctypes.c_size_t, vp]
         L.cp_attn_status_string.argtypes = [i32]
         L.cp_attn_status_string.restype = ctypes.c_char_p
         L.cp_attn_last_error.argtypes = []
@@ -270,6 +275,36 @@ def cp_attn_rank_forward(desc: Desc, q, k_blocks: Sequence, v_blocks: Sequence, 
                                       _ptr(lse_out), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), cs, xs, int(flags),
                                       profiler.handle if profiler is not None else None))
+
+
+def cp_attn_ulysses_workspace_bytes(desc: Desc) -> int:
+    n = int(lib().cp_attn_ulysses_workspace_bytes(desc.ref))
+    if n == 0:
+        raise CpAttnError(CP_ERR_INVALID_ARG, last_error())
+    return n
+
+
+def cp_attn_ulysses_forward(desc: Desc, q_shards: Sequence, k_shards: Sequence, v_shards: Sequence,
+                            o_shards: Sequence, m_out=None, l_out=None, lse_out=None, workspace=None,
+                            stream=None) -> None:
+    import torch
+    c = desc.c
+    big = (c.B, c.L, c.H, c.d)
+    N = c.N
+    vec = (c.B, c.H // N if N else 0, c.L * N)
+    dt = _io_dtype(desc)
+    if not (len(q_shards) == len(k_shards) == len(v_shards) == len(o_shards) == N):
+        raise ValueError(f"need N={N} entries in q_shards, k_shards, v_shards and o_shards")
+    for t in list(q_shards) + list(k_shards) + list(v_shards) + list(o_shards):
+        _check_tensor(t, "shard", big, dt)
+    for n, t in (("m_out", m_out), ("l_out", l_out), ("lse_out", lse_out)):
+        _check_tensor(t, n, vec, torch.float32)
+    if workspace is None or not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+        raise ValueError("workspace must be a device tensor")
+    arr = lambda ts: (ctypes.c_void_p * N)(*[_ptr(t) for t in ts])  # noqa: E731
+    _check(lib().cp_attn_ulysses_forward(desc.ref, arr(q_shards), arr(k_shards), arr(v_shards), arr(o_shards),
+                                         _ptr(m_out), _ptr(l_out), _ptr(lse_out), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def cp_attn_bwd_delta(desc: Desc, o, d_o, delta, stream=None) -> None:

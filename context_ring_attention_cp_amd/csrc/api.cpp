@@ -662,3 +662,106 @@ void cp_attn_profiler_destroy(cp_attn_profiler* prof) {
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// all-to-all (Ulysses) context parallelism, one rank's share
+// ---------------------------------------------------------------------------
+namespace {
+
+static_assert(kMaxShards == CP_MAX_RING, "regroup pointer table sized to the ring limit");
+
+// The description of the attention a rank runs after the first all-to-all:
+// one block of the whole sequence (N = 1, L = S) on H/N heads.
+cp_status ulysses_full_desc(const cp_attn_desc* d, cp_attn_desc* full) {
+  cp_status st = check_desc(d);
+  if (st != CP_OK) return st;
+  if (d->H % d->N != 0)
+    return fail(CP_ERR_INVALID_ARG, "H=%d is not a multiple of N=%d (each rank takes H/N heads)", d->H, d->N);
+  *full = *d;
+  full->N = 1;
+  full->rank = 0;
+  full->L = d->L * d->N;
+  full->H = d->H / d->N;
+  return check_desc(full);
+}
+
+size_t ulysses_full_bytes(const cp_attn_desc* full) {
+  return round_up((size_t)full->B * full->L * full->H * full->d * elt_bytes(full->dtype), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t cp_attn_ulysses_workspace_bytes(const cp_attn_desc* desc) {
+  g_last_error.clear();
+  cp_attn_desc full;
+  if (ulysses_full_desc(desc, &full) != CP_OK) return 0;
+  return 4 * ulysses_full_bytes(&full);
+}
+
+cp_status cp_attn_ulysses_forward(const cp_attn_desc* desc, const void* const* q_shards,
+                                  const void* const* k_shards, const void* const* v_shards,
+                                  void* const* o_shards, float* m_out, float* l_out, float* lse_out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  cp_attn_desc full;
+  cp_status st = ulysses_full_desc(desc, &full);
+  if (st != CP_OK) return st;
+  if (!q_shards || !k_shards || !v_shards || !o_shards)
+    return fail(CP_ERR_INVALID_ARG, "q_shards/k_shards/v_shards/o_shards is NULL");
+  for (int32_t i = 0; i < desc->N; ++i) {
+    if ((st = check_tensor(q_shards[i], "q_shards[i]")) != CP_OK || (st = check_tensor(k_shards[i], "k_shards[i]")) != CP_OK ||
+        (st = check_tensor(v_shards[i], "v_shards[i]")) != CP_OK || (st = check_tensor(o_shards[i], "o_shards[i]")) != CP_OK)
+      return st;
+  }
+  if ((st = check_vec(m_out, "m_out", true)) != CP_OK || (st = check_vec(l_out, "l_out", true)) != CP_OK ||
+      (st = check_vec(lse_out, "lse_out", true)) != CP_OK)
+    return st;
+  const size_t fb = ulysses_full_bytes(&full);
+  if (!workspace) return fail(CP_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(CP_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < 4 * fb) return fail(CP_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, 4 * fb);
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  void* qf = ws;
+  void* kf = ws + fb;
+  void* vf = ws + 2 * fb;
+  void* of = ws + 3 * fb;
+  RegroupArgs ra;
+  std::memset(&ra, 0, sizeof(ra));
+  ra.B = desc->B;
+  ra.L = desc->L;
+  ra.S = full.L;
+  ra.N = desc->N;
+  ra.H = desc->H;
+  ra.Hn = full.H;
+  ra.h0 = desc->rank * full.H;
+  ra.d = desc->d;
+  ra.elt = (int32_t)elt_bytes(desc->dtype);
+  hipError_t e = hipSuccess;
+  // step 1: the first all-to-all, as seen by this rank (its heads of every shard)
+  const void* const* srcs[3] = {q_shards, k_shards, v_shards};
+  void* dsts[3] = {qf, kf, vf};
+  for (int x = 0; x < 3; ++x) {
+    for (int32_t i = 0; i < desc->N; ++i) ra.shards[i] = const_cast<void*>(srcs[x][i]);
+    ra.full = dsts[x];
+    if ((e = launch_a2a_gather(ra, s)) != hipSuccess) return hip_fail(e, "all-to-all gather launch");
+  }
+  // step 2: attention over the whole sequence for this rank's heads
+  BlockArgs a = block_args(&full, 0, qf, kf, vf);
+  a.flags = F_WRITE_FINAL;
+  a.out = of;
+  a.m_out = m_out;
+  a.l_out = l_out;
+  a.lse_out = lse_out;
+  if ((e = launch_block(&full, a, s)) != hipSuccess) return hip_fail(e, "block kernel launch");
+  // step 3: the second all-to-all, as sent by this rank (its heads of every shard)
+  for (int32_t i = 0; i < desc->N; ++i) ra.shards[i] = o_shards[i];
+  ra.full = of;
+  if ((e = launch_a2a_scatter(ra, s)) != hipSuccess) return hip_fail(e, "all-to-all scatter launch");
+  return CP_OK;
+}
+
+}  // extern "C"

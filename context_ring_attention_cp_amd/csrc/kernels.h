@@ -110,4 +110,18 @@ hipError_t launch_bwd_delta(const DeltaArgs& a, int d, hipStream_t s);
 hipError_t launch_bwd_blocks(const BwdArgs& a, int d, hipStream_t s);   // dq kernel, then dk/dv kernel
 hipError_t launch_zero(float* p, int64_t n, hipStream_t s);            // n a multiple of 4
 
+// Regrouping of all-to-all (Ulysses) context parallelism between the N
+// sequence shards [B, L, H, d] and the whole sequence of one rank's head
+// group [h0, h0 + Hn), stored [B, S, Hn, d] (S = N L).  Element bytes elt; Hn d
+// elt a multiple of 16 and every pointer 16-byte aligned.
+constexpr int kMaxShards = 64;
+struct RegroupArgs {
+  void* shards[kMaxShards];   // gather: read; scatter: written (only the group's heads)
+  void* full;                 // gather: written; scatter: read
+  int64_t B, L, S;
+  int32_t N, H, Hn, h0, d, elt;
+};
+hipError_t launch_a2a_gather(const RegroupArgs& a, hipStream_t s);
+hipError_t launch_a2a_scatter(const RegroupArgs& a, hipStream_t s);
+
 }  // namespace cpattn

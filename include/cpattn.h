@@ -181,6 +181,46 @@ cp_status cp_attn_rank_forward(const cp_attn_desc* desc, const void* q,
                                void* workspace, size_t workspace_bytes, void* compute_stream,
                                void* copy_stream, int32_t flags, cp_attn_profiler* prof);
 
+/* ---- All-to-all (Ulysses) context parallelism, one rank's share ----------
+ * The second scheme of the compassingai.com page (section
+ * "方案二：All-to-All（全交換）"): the ranks hold the same sequence shards as
+ * in the ring; an all-to-all regroups Q, K, V from split-by-sequence to
+ * split-by-head, each rank computes attention over the whole sequence for its
+ * heads, and a second all-to-all regroups the outputs back to
+ * split-by-sequence.  Under a causal or document mask the invalid region is
+ * masked, not skipped (same page, section "技術路線對比"); the two
+ * exchanges move about 2 x S H d elements (section "通訊量分析").  Rank r
+ * takes the contiguous head group [r H/N, (r+1) H/N); desc->H must be a
+ * multiple of desc->N.  The masks use the same global positions as the ring
+ * (shard i covers [i L, (i+1) L)). */
+
+/* Bytes of workspace cp_attn_ulysses_forward needs: the whole sequence of
+ * the rank's heads for Q, K, V and the output, 4 x B S (H/N) d elements of
+ * desc->dtype, 256-byte aligned pieces.  Returns 0 if the desc is invalid or
+ * H is not a multiple of N (cp_attn_last_error() says why). */
+size_t cp_attn_ulysses_workspace_bytes(const cp_attn_desc* desc);
+
+/* The share of rank r = desc->rank, with the two all-to-alls simulated on one
+ * GPU: q_shards[i], k_shards[i], v_shards[i] (HOST arrays of N device
+ * pointers, [B, L, H, d] of desc->dtype each) are what rank i holds; this
+ * call reads only heads [r H/N, (r+1) H/N) of them (the first exchange, as
+ * received by rank r), runs the attention of the whole sequence S = N L on
+ * those heads (one launch of the block kernel), and writes the result into
+ * the same heads of o_shards[i] (HOST array of N device pointers, [B, L, H,
+ * d] of desc->dtype; the second exchange, as sent by rank r), leaving the
+ * other heads of o_shards untouched.  Calling it for every rank fills all of
+ * o_shards.
+ *   m_out, l_out, lse_out : device [B, H/N, S] float32 for rank r's heads over
+ *                  the whole sequence (natural-log units), each may be NULL;
+ *   workspace    : device, >= cp_attn_ulysses_workspace_bytes(desc) bytes,
+ *                  256-byte aligned, not shared with a concurrent call;
+ *   stream       : all work is enqueued on it, in order.
+ * Errors: CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED, CP_ERR_WORKSPACE, CP_ERR_HIP. */
+cp_status cp_attn_ulysses_forward(const cp_attn_desc* desc, const void* const* q_shards,
+                                  const void* const* k_shards, const void* const* v_shards,
+                                  void* const* o_shards, float* m_out, float* l_out, float* lse_out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- Backward of one rank shard ------------------------------------------
  * The backward walks the ring's K/V blocks again and recomputes what the
  * forward did not keep (compassingai.com page, section "反向傳播"; the Q, K, V

@@ -313,3 +313,42 @@ def test_backward_argument_errors():
     for args, msg in cases_rank:
         assert _status(lib.cp_attn_rank_backward, *args) == B.CP_ERR_INVALID_ARG, (msg, B.last_error())
         assert msg in B.last_error(), (msg, B.last_error())
+
+
+def test_ulysses_workspace_bytes():
+    """Q, K, V and the output of the whole sequence for H/N heads."""
+    d = _desc(N=4, L=32768, rank=3, H=32)
+    piece = 1 * 131072 * 8 * 128 * 2
+    assert B.cp_attn_ulysses_workspace_bytes(d) == 4 * piece
+    d32 = _desc(N=3, L=100, rank=0, H=6, dtype="f32", d=64)
+    piece = 300 * 2 * 64 * 4
+    assert 4 * piece <= B.cp_attn_ulysses_workspace_bytes(d32) <= 4 * (piece + 255)
+    assert B.lib().cp_attn_ulysses_workspace_bytes(_desc(N=4, H=6).ref) == 0
+    assert "multiple of N" in B.last_error()
+
+
+def test_ulysses_argument_errors():
+    lib = B.lib()
+    d = _desc(N=4, H=8)
+    P = ctypes.c_void_p
+    sh = (P * 4)(FAKE, FAKE + 256, FAKE + 512, FAKE + 768)
+    need = B.cp_attn_ulysses_workspace_bytes(d)
+    S1 = 0x1000
+    cases = [
+        ((_desc(N=4, H=6).ref, sh, sh, sh, sh, None, None, None, FAKE, need, S1), B.CP_ERR_INVALID_ARG, "multiple of N"),
+        ((d.ref, None, sh, sh, sh, None, None, None, FAKE, need, S1), B.CP_ERR_INVALID_ARG, "NULL"),
+        ((d.ref, sh, sh, sh, None, None, None, None, FAKE, need, S1), B.CP_ERR_INVALID_ARG, "NULL"),
+        ((d.ref, sh, (P * 4)(FAKE, FAKE, None, FAKE), sh, sh, None, None, None, FAKE, need, S1),
+         B.CP_ERR_INVALID_ARG, "k_shards[i]"),
+        ((d.ref, sh, sh, sh, (P * 4)(FAKE, FAKE + 8, FAKE, FAKE), None, None, None, FAKE, need, S1),
+         B.CP_ERR_INVALID_ARG, "o_shards[i] is not 16-byte aligned"),
+        ((d.ref, sh, sh, sh, sh, None, None, FAKE + 2, FAKE, need, S1), B.CP_ERR_INVALID_ARG, "lse_out"),
+        ((d.ref, sh, sh, sh, sh, None, None, None, None, need, S1), B.CP_ERR_WORKSPACE, "workspace is NULL"),
+        ((d.ref, sh, sh, sh, sh, None, None, None, FAKE + 16, need, S1), B.CP_ERR_WORKSPACE, "256-byte"),
+        ((d.ref, sh, sh, sh, sh, None, None, None, FAKE, need - 1, S1), B.CP_ERR_WORKSPACE, "needed"),
+        ((_desc(N=4, H=8, d=96).ref, sh, sh, sh, sh, None, None, None, FAKE, need, S1), B.CP_ERR_UNSUPPORTED, "head dim"),
+    ]
+    for args, status, msg in cases:
+        st = _status(lib.cp_attn_ulysses_forward, *args)
+        assert st == status, (msg, st, B.last_error())
+        assert msg in B.last_error(), (msg, B.last_error())
