@@ -52,6 +52,8 @@
 namespace cpattn {
 namespace {
 
+template <int V> struct IntTag { static constexpr int value = V; };
+
 using namespace dev;
 
 
@@ -227,34 +229,54 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   const int tr_row = (lane & 15) >> 2;                         // + 16 kstep + 8 g + 4 h
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32 dt
 
-  // S^T = K Q^T of one tile; the K operands of head-dim step s+2 are read
-  // while step s multiplies.
-  auto qk = [&](const bf16* __restrict__ Ks, floatx16 (&sacc)[NT]) {
+  // LDS operands of the compute phase, in the order the MFMAs consume them:
+  // slots 0 .. NQK-1 are the K rows of S^T = K Q^T (head-dim step j / NT,
+  // key sub-tile j % NT), slots NQK .. NQK+NPM-1 the V^T operands of
+  // O^T += V^T P^T (key step k / NDT, head-dim tile k % NDT, from the
+  // transpose loads).
+  constexpr int NQK = NS * NT;
+  constexpr int NPM = NPV * NDT;
+  constexpr int RA = 6;                                        // operands read ahead of their MFMA
+  auto rd_k = [&](const bf16* __restrict__ Ks, int j) {
+    const int row = 32 * (j % NT) + krow_l;
+    return *(const bf16x8*)(Ks + row * D + 8 * ((2 * (j / NT) + g) ^ swz_k<D>(row)));
+  };
+  auto rd_v = [&](const bf16* __restrict__ Vs, int k) {
+    const int col = 32 * (k % NDT) + tr_col;
+    const int row0 = 16 * (k / NDT) + 8 * g + tr_row;
+    const int row1 = row0 + 4;
+    const short4v x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4v*)(Vs + row0 * D + 8 * ((col >> 3) ^ swz_v<D>(row0)) + (col & 7)));
+    const short4v x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4v*)(Vs + row1 * D + 8 * ((col >> 3) ^ swz_v<D>(row1)) + (col & 7)));
+    return __builtin_bit_cast(bf16x8, short8v{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
+  };
+  // The compute phase: S^T = K Q^T of one tile (QK) and O^T += V^T P^T of the
+  // previous one (PV), as one stream of MFMAs.  Each MFMA's operand is read
+  // RA MFMAs earlier (LDS returns in order, so the reads go out in the order
+  // they are consumed, and the V reads start under the last QK MFMAs); the
+  // scheduling fences keep that order.
+  auto compute = [&](const bf16* __restrict__ Ks, const bf16* __restrict__ Vs, floatx16 (&sacc)[NT],
+                     const bf16x8 (&pb)[NPV], auto qk_tag, auto pv_tag) {
+    constexpr bool QK = decltype(qk_tag)::value != 0, PV = decltype(pv_tag)::value != 0;
+    constexpr int J0 = QK ? 0 : NQK, J1 = PV ? NQK + NPM : NQK;
+    auto rd = [&](int j) { return j < NQK ? rd_k(Ks, j) : rd_v(Vs, j - NQK); };
+    if constexpr (QK) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) sacc[t] = floatx16{};
-    auto rd = [&](int s, int t) {
-      const int row = 32 * t + krow_l;
-      return *(const bf16x8*)(Ks + row * D + 8 * ((2 * s + g) ^ swz_k<D>(row)));
-    };
-    bf16x8 kb[3][NT];
-#pragma unroll
-    for (int s = 0; s < 2 && s < NS; ++s)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) kb[s][t] = rd(s, t);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (s + 2 < NS)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) kb[(s + 2) % 3][t] = rd(s + 2, t);
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[s % 3][t], qreg[s], sacc[t], 0, 0, 0);
+      for (int t = 0; t < NT; ++t) sacc[t] = floatx16{};
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NT, 0);
+    bf16x8 ring[RA];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (s + 2 < NS) __builtin_amdgcn_sched_group_barrier(0x100, NT, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);
+    for (int j = J0; j < J0 + RA && j < J1; ++j) ring[j - J0] = rd(j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = J0; j < J1; ++j) {
+      const bf16x8 op = ring[(j - J0) % RA];
+      if (j < NQK) sacc[j % NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qreg[j / NT], sacc[j % NT], 0, 0, 0);
+      else oacc[(j - NQK) % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, pb[(j - NQK) / NDT],
+                                                                          oacc[(j - NQK) % NDT], 0, 0, 0);
+      if (j + RA < J1) ring[(j - J0) % RA] = rd(j + RA);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -353,24 +375,6 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
       }
     }
   };
-  // O^T += V^T P^T for one tile.
-  auto pv = [&](const bf16* __restrict__ Vs, bf16x8 (&pb)[NPV]) {
-#pragma unroll
-    for (int ks = 0; ks < NPV; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int col = 32 * dt + tr_col;
-        const int row0 = 16 * ks + 8 * g + tr_row;
-        const int row1 = row0 + 4;
-        const short4v x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4v*)(Vs + row0 * D + 8 * ((col >> 3) ^ swz_v<D>(row0)) + (col & 7)));
-        const short4v x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4v*)(Vs + row1 * D + 8 * ((col >> 3) ^ swz_v<D>(row1)) + (col & 7)));
-        const short8v x = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), pb[ks], oacc[dt], 0, 0, 0);
-      }
-  };
-
   if (kt_begin < kt_end) {
     const int grp = w >> 2;
     auto stage = [&](int u) { return (u - kt_begin) & (kStages - 1); };
@@ -384,17 +388,20 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
     if (grp == 1) __syncthreads();                   // group 1 runs one phase behind
     floatx16 sacc[NT];
     bf16x8 pb[NPV];
-    for (int u = kt_begin; u <= kt_end; ++u) {
-      // compute phase
-      if (u < kt_end) qk(smem[stage(u)][0], sacc);
-      if (u > kt_begin) pv(smem[stage(u - 1)][1], pb);
+    // One step u: the compute phase (QK of tile u unless u == kt_end, PV of
+    // tile u-1 unless u == kt_begin), then the softmax phase of tile u.  The
+    // first and last steps are peeled off the loop, so that the loop body
+    // holds one form of the compute phase.
+    auto step = [&](int u, auto qk_tag, auto pv_tag) {
+      constexpr bool QK = decltype(qk_tag)::value != 0;
+      compute(smem[stage(u)][0], smem[stage(u - 1)][1], sacc, pb, qk_tag, pv_tag);
       lds_read_barrier();
       // softmax phase; group 0 first starts the fetch of tile u+2
       const bool more = u + 2 < kt_end;
       if (grp == 0 && more) {
         fetch(u + 2, stage(u + 2));
       }
-      if (u < kt_end) {
+      if constexpr (QK) {
         if (need_mask(u)) apply_mask(u, sacc);
         rescale(row_max(sacc));
         exp_sum(sacc, pb);
@@ -405,7 +412,10 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
       else __builtin_amdgcn_s_waitcnt(0x0070);                             // vmcnt(0) lgkmcnt(0)
       __builtin_amdgcn_s_barrier();
       __asm__ volatile("" ::: "memory");
-    }
+    };
+    step(kt_begin, IntTag<1>{}, IntTag<0>{});
+    for (int u = kt_begin + 1; u < kt_end; ++u) step(u, IntTag<1>{}, IntTag<1>{});
+    step(kt_end, IntTag<0>{}, IntTag<1>{});
     if (grp == 0) __syncthreads();                   // same barrier count for both groups
   }
 
