@@ -33,7 +33,7 @@ EXPORTED = [
     "cp_attn_profiler_create", "cp_attn_profiler_reset", "cp_attn_profiler_read",
     "cp_attn_profiler_destroy", "cp_attn_status_string", "cp_attn_last_error",
     "cp_attn_bwd_delta", "cp_attn_block_backward", "cp_attn_rank_backward",
-    "cp_attn_ulysses_workspace_bytes", "cp_attn_ulysses_forward",
+    "cp_attn_ulysses_workspace_bytes", "cp_attn_ulysses_forward", "cp_attn_quantize_fp8",
 ]
 
 
@@ -93,6 +93,7 @@ def lib() -> ctypes.CDLL:
         L.cp_attn_ulysses_workspace_bytes.restype = ctypes.c_size_t
         L.cp_attn_ulysses_forward.argtypes = [dp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                               ctypes.POINTER(vp), f32p, f32p, f32p, vp, ctypes.c_size_t, vp]
+        L.cp_attn_quantize_fp8.argtypes = [dp, vp, vp, f32p, vp]
         L.cp_attn_status_string.argtypes = [i32]
         L.cp_attn_status_string.restype = ctypes.c_char_p
         L.cp_attn_last_error.argtypes = []
@@ -305,6 +306,19 @@ def cp_attn_ulysses_forward(desc: Desc, q_shards: Sequence, k_shards: Sequence, 
     _check(lib().cp_attn_ulysses_forward(desc.ref, arr(q_shards), arr(k_shards), arr(v_shards), arr(o_shards),
                                          _ptr(m_out), _ptr(l_out), _ptr(lse_out), _ptr(workspace),
                                          workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def cp_attn_quantize_fp8(desc: Desc, x, codes, scales, stream=None) -> None:
+    """x: bf16 [B, L, H, d]; codes: uint8 [B, L, H, d]; scales: float32 [B, H]."""
+    import torch
+    c = desc.c
+    big = (c.B, c.L, c.H, c.d)
+    _check_tensor(x, "x", big, torch.bfloat16)
+    _check_tensor(codes, "codes", big, torch.uint8)
+    _check_tensor(scales, "scales", (c.B, c.H), torch.float32)
+    if codes is None or scales is None:
+        raise ValueError("codes and scales are required")
+    _check(lib().cp_attn_quantize_fp8(desc.ref, _ptr(x), _ptr(codes), _ptr(scales), _stream(stream)))
 
 
 def cp_attn_bwd_delta(desc: Desc, o, d_o, delta, stream=None) -> None:

@@ -764,4 +764,27 @@ cp_status cp_attn_ulysses_forward(const cp_attn_desc* desc, const void* const* q
   return CP_OK;
 }
 
+cp_status cp_attn_quantize_fp8(const cp_attn_desc* desc, const void* x, void* codes, float* scales, void* stream) {
+  g_last_error.clear();
+  cp_status st = check_desc(desc);
+  if (st != CP_OK) return st;
+  if (desc->dtype != CP_BF16) return fail(CP_ERR_UNSUPPORTED, "cp_attn_quantize_fp8 takes bf16 input (dtype=%d)", desc->dtype);
+  if ((st = check_tensor(x, "x")) != CP_OK) return st;
+  if (!codes) return fail(CP_ERR_INVALID_ARG, "codes is NULL");
+  if (!aligned(codes, 8)) return fail(CP_ERR_INVALID_ARG, "codes is not 8-byte aligned");
+  if ((st = check_vec(scales, "scales", false)) != CP_OK) return st;
+  if ((long double)desc->L / 256 + 1 > 2147483647.0L || (long double)desc->B * desc->H > 65535.0L)
+    return fail(CP_ERR_UNSUPPORTED, "grid of the quantisation too large (B*H=%lld)", (long long)desc->B * desc->H);
+  QuantArgs a;
+  a.x = x;
+  a.codes = codes;
+  a.scales = scales;
+  a.L = desc->L;
+  a.B = desc->B;
+  a.H = desc->H;
+  const hipError_t e = launch_quantize_fp8(a, desc->d, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "quantisation launch");
+  return CP_OK;
+}
+
 }  // extern "C"

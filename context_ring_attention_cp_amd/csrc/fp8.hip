@@ -1,0 +1,115 @@
+// FP8 (OCP e4m3) quantisation of a [B, L, H, d] bf16 block for gfx950.
+//
+// One scale per (batch, head): amax = max |x| over the block's tokens and
+// head dim, scale = amax / 448 and inv = 448 / amax (float32, correctly
+// rounded; both 1 when amax = 0); code(x) = e4m3 nearest to
+// clamp(x * inv, -448, 448), ties to even (v_cvt_pk_fp8_f32, which rounds to
+// nearest even but turns magnitudes from 464 up into NaN, hence the clamp).
+// The compassingai.com context-parallelism page notes that the bytes CP moves
+// depend on FP8 transfer (section "通訊量分析"); the format and scaling are
+// this library's choice.
+//
+// Four launches, all HBM-bound streaming except the last: fill the amax slots
+// with 0, the per-workgroup maxima merged with a vector atomicMax on the
+// float bits (order-preserving for non-negative floats), the codes, then the
+// scales.  Each thread handles 8 consecutive elements of one token row of one
+// head; a workgroup covers kRowsPerWg rows of one (b, h).
+#include "kernels.h"
+
+#include <stdint.h>
+
+namespace cpattn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerWg = 256;
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__global__ __launch_bounds__(kThreads) void fill_kernel(float* p, int64_t n, float v) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// grid: x = row chunk of kRowsPerWg rows, y = b * H + h
+template <int D>
+__global__ __launch_bounds__(kThreads) void amax_kernel(QuantArgs a) {
+  constexpr int TPR = D / 8;                        // threads per row
+  constexpr int RPP = kThreads / TPR;               // rows per pass
+  const int bh = blockIdx.y;
+  const int b = bh / a.H, h = bh % a.H;
+  const int64_t r0 = (int64_t)blockIdx.x * kRowsPerWg;
+  const int c = threadIdx.x % TPR;
+  float m = 0.f;
+  for (int rr = threadIdx.x / TPR; rr < kRowsPerWg; rr += RPP) {
+    const int64_t t = r0 + rr;
+    if (t < a.L) {
+      const bf16x8 x = *(const bf16x8*)((const bf16*)a.x + (((int64_t)b * a.L + t) * a.H + h) * D + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)x[e]));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  __shared__ float wm[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float mm = wm[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) mm = fmaxf(mm, wm[i]);
+    atomicMax((unsigned int*)&a.scales[bh], __float_as_uint(mm));
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
+  constexpr int TPR = D / 8;
+  constexpr int RPP = kThreads / TPR;
+  const int bh = blockIdx.y;
+  const int b = bh / a.H, h = bh % a.H;
+  const float amax = a.scales[bh];                  // still the amax here
+  const float inv = amax > 0.f ? 448.f / amax : 1.f;
+  const int64_t r0 = (int64_t)blockIdx.x * kRowsPerWg;
+  const int c = threadIdx.x % TPR;
+  for (int rr = threadIdx.x / TPR; rr < kRowsPerWg; rr += RPP) {
+    const int64_t t = r0 + rr;
+    if (t >= a.L) break;
+    const int64_t off = (((int64_t)b * a.L + t) * a.H + h) * D + 8 * c;
+    const bf16x8 x = *(const bf16x8*)((const bf16*)a.x + off);
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = __builtin_amdgcn_fmed3f((float)x[e] * inv, -448.f, 448.f);
+    uint32_t w0 = 0, w1 = 0;
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], w0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], w1, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
+    *(uint2*)((uint8_t*)a.codes + off) = uint2{w0, w1};
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void scale_kernel(float* s, int n) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) s[i] = s[i] > 0.f ? s[i] / 448.f : 1.f;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_fp8(const QuantArgs& a, int d, hipStream_t s) {
+  const int n = a.B * a.H;
+  const dim3 grid((unsigned)((a.L + kRowsPerWg - 1) / kRowsPerWg), (unsigned)n);
+  fill_kernel<<<(n + kThreads - 1) / kThreads, kThreads, 0, s>>>(a.scales, n, 0.f);
+  if (d == 128) {
+    amax_kernel<128><<<grid, kThreads, 0, s>>>(a);
+    quantize_kernel<128><<<grid, kThreads, 0, s>>>(a);
+  } else {
+    amax_kernel<64><<<grid, kThreads, 0, s>>>(a);
+    quantize_kernel<64><<<grid, kThreads, 0, s>>>(a);
+  }
+  scale_kernel<<<(n + kThreads - 1) / kThreads, kThreads, 0, s>>>(a.scales, n);
+  return hipGetLastError();
+}
+
+}  // namespace cpattn

@@ -124,4 +124,15 @@ struct RegroupArgs {
 hipError_t launch_a2a_gather(const RegroupArgs& a, hipStream_t s);
 hipError_t launch_a2a_scatter(const RegroupArgs& a, hipStream_t s);
 
+// FP8 (e4m3) quantisation of a bf16 block [B, L, H, d] with one scale per
+// (b, h): codes [B, L, H, d] bytes, scales [B, H] float32 (amax / 448).
+struct QuantArgs {
+  const void* x;
+  void* codes;
+  float* scales;
+  int64_t L;
+  int32_t B, H;
+};
+hipError_t launch_quantize_fp8(const QuantArgs& a, int d, hipStream_t s);
+
 }  // namespace cpattn

@@ -221,6 +221,23 @@ cp_status cp_attn_ulysses_forward(const cp_attn_desc* desc, const void* const* q
                                   void* const* o_shards, float* m_out, float* l_out, float* lse_out,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- FP8 (e4m3) ---------------------------------------------------------
+ * The compassingai.com page notes that the bytes CP moves depend on whether
+ * blocks travel compressed or in FP8 (section "通訊量分析") and that
+ * FlashAttention-3 computes attention in FP8 (section "技術演進史").  This
+ * library's FP8 format is OCP E4M3 (largest value 448) with one float32 scale
+ * per (batch, head) and block: scale = amax / 448 over the block's tokens and
+ * head dim, inverse 448 / amax (both correctly rounded; 1 when amax = 0); a
+ * value x is stored as the e4m3 code nearest to clamp(x * inverse, +-448),
+ * ties to even, and stands for decode(code) * scale. */
+
+/* Quantise one bf16 block x (device [B, L, H, d] with desc's B, L, H, d) to
+ * codes (device [B, L, H, d] bytes, 8-byte aligned) and scales (device [B, H]
+ * float32).  x must be finite.  Four launches on stream (fill, per-head
+ * maxima, codes, scales); scales is overwritten.
+ * Errors: CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED (desc->dtype not bf16), CP_ERR_HIP. */
+cp_status cp_attn_quantize_fp8(const cp_attn_desc* desc, const void* x, void* codes, float* scales, void* stream);
+
 /* ---- Backward of one rank shard ------------------------------------------
  * The backward walks the ring's K/V blocks again and recomputes what the
  * forward did not keep (compassingai.com page, section "反向傳播"; the Q, K, V

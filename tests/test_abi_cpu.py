@@ -352,3 +352,21 @@ def test_ulysses_argument_errors():
         st = _status(lib.cp_attn_ulysses_forward, *args)
         assert st == status, (msg, st, B.last_error())
         assert msg in B.last_error(), (msg, B.last_error())
+
+
+def test_quantize_fp8_argument_errors():
+    lib = B.lib()
+    d = _desc()
+    S1 = 0x1000
+    cases = [
+        ((_desc(dtype="f32").ref, FAKE, FAKE, FAKE, S1), B.CP_ERR_UNSUPPORTED, "bf16"),
+        ((d.ref, None, FAKE, FAKE, S1), B.CP_ERR_INVALID_ARG, "x is NULL"),
+        ((d.ref, FAKE, None, FAKE, S1), B.CP_ERR_INVALID_ARG, "codes is NULL"),
+        ((d.ref, FAKE, FAKE + 4, FAKE, S1), B.CP_ERR_INVALID_ARG, "8-byte"),
+        ((d.ref, FAKE, FAKE, None, S1), B.CP_ERR_INVALID_ARG, "scales is NULL"),
+        ((d.ref, FAKE, FAKE, FAKE + 2, S1), B.CP_ERR_INVALID_ARG, "scales is not 4-byte"),
+    ]
+    for args, status, msg in cases:
+        st = _status(lib.cp_attn_quantize_fp8, *args)
+        assert st == status, (msg, st, B.last_error())
+        assert msg in B.last_error(), (msg, B.last_error())
