@@ -28,18 +28,29 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk (the published 2.5 PF)
+PEAK_FP8_TFLOPS = 5033.2      # MI355X dense FP8 MFMA: twice the bf16 rate (the published 5.0 PF)
 PEAK_HBM_GBS = 8000.0
-KERNEL_SRCS = [os.path.join(ROOT, "context_ring_attention_cp_amd", "csrc", f)
-               for f in ("attn_mfma.hip", "gfx950_util.h", "kernels.h")]
-TRAFFIC_JSON = os.path.join(ROOT, "profiles", "attn_block_bf16__causal_128k_last_rank.traffic.json")
-ATTN_KERNEL = "attn_block_bf16_kernel<128>"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
+_BLK = 32768 * 32 * 128                 # elements of one K or V block of the 128K example
+# Per profiled kernel: its name in the traces, the sources it is compiled
+# from, the committed PMC summary, the bytes of one ring-receive copy of the
+# same run (the counters' calibration) and the command the runs profile.
+KERNELS = {
+    "bf16": dict(name="attn_block_bf16_kernel<128>", srcs=("attn_mfma.hip", "gfx950_util.h", "kernels.h"),
+                 json="attn_block_bf16__causal_128k_last_rank.traffic.json", copy_bytes=2 * _BLK,
+                 cmd="python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-secondary"),
+    "fp8": dict(name="attn_block_fp8_kernel<128>", srcs=("attn_fp8.hip", "gfx950_util.h", "kernels.h"),
+                json="attn_block_fp8__causal_128k_last_rank.traffic.json", copy_bytes=_BLK,
+                cmd="python3 bench.py --fp8-only --steps 1 --warmup 0"),
+}
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", KERNELS["bf16"]["json"])
 
 
-def kernel_sha256() -> str:
-    """SHA-256 over the sources the forward block kernel is compiled from."""
+def kernel_sha256(which: str = "bf16") -> str:
+    """SHA-256 over the sources a forward block kernel is compiled from."""
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
+    for f in KERNELS[which]["srcs"]:
+        path = os.path.join(ROOT, "context_ring_attention_cp_amd", "csrc", f)
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -57,16 +68,18 @@ def _pmc_rows(d: str, counter: str):
     return sorted(rows)
 
 
-def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int, out: str) -> dict:
-    """HBM traffic of the attention kernel from a FETCH_SIZE run and a
-    WRITE_SIZE run (KiB per dispatch) of `bench.py --steps 1 --warmup 0`.
-    Each counter is scaled by what it reads for the ring-receive copy kernels
-    of the same run, which move `copy_bytes` each (one K or V block)."""
+def summarize_pmc(fetch_dir: str, write_dir: str, which: str = "bf16") -> dict:
+    """HBM traffic of an attention kernel from a FETCH_SIZE run and a
+    WRITE_SIZE run (KiB per dispatch) of its one-step bench command.  Each
+    counter is scaled by what it reads for the ring-receive copy kernels of
+    the same run, which move one K or V block each."""
+    kern = KERNELS[which]
+    copy_bytes, attn_kernel = kern["copy_bytes"], kern["name"]
     res = {}
     for name, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = _pmc_rows(d, counter)
         cal = [v for _, k, v in rows if COPY_KERNEL in k and abs(v * 1024 - copy_bytes) < 0.6 * copy_bytes]
-        att = [v for _, k, v in rows if ATTN_KERNEL in k]
+        att = [v for _, k, v in rows if attn_kernel in k]
         if not cal or not att:
             raise SystemExit(f"{counter}: calibration copies {len(cal)}, attention dispatches {len(att)}")
         factor = copy_bytes / (sum(cal) / len(cal) * 1024)
@@ -74,25 +87,25 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int, out: str) -> 
     n = min(len(res["fetch"]["kib_per_dispatch"]), len(res["write"]["kib_per_dispatch"]))
     per = [res["fetch"]["kib_per_dispatch"][i] * 1024 * res["fetch"]["factor"]
            + res["write"]["kib_per_dispatch"][i] * 1024 * res["write"]["factor"] for i in range(n)]
-    summary = {"kernel": ATTN_KERNEL, "kernel_source_sha256": kernel_sha256(), "dispatches": n,
+    summary = {"kernel": attn_kernel, "kernel_source_sha256": kernel_sha256(which), "dispatches": n,
                "traffic_bytes_per_dispatch": per, "traffic_bytes_mean": sum(per) / n,
                "fetch": res["fetch"], "write": res["write"], "calibration_copy_bytes": copy_bytes,
                "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o <name> -- "
-                          "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-secondary"}
-    with open(out, "w") as f:
+                          + kern["cmd"]}
+    with open(os.path.join(ROOT, "profiles", kern["json"]), "w") as f:
         json.dump(summary, f, indent=1)
     return summary
 
 
-def measured_traffic():
+def measured_traffic(which: str = "bf16"):
     """Mean HBM bytes per attention dispatch from the committed PMC summary,
     or None if it was taken on a different kernel source."""
     try:
-        with open(TRAFFIC_JSON) as f:
+        with open(os.path.join(ROOT, "profiles", KERNELS[which]["json"])) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != kernel_sha256():
+    if t.get("kernel_source_sha256") != kernel_sha256(which):
         return None
     return t["traffic_bytes_mean"]
 
@@ -110,6 +123,10 @@ def parse():
                     help="query rows of one head timed on the CPU oracle")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two rocprofv3 --pmc runs and exit (no GPU)")
+    ap.add_argument("--pmc-kernel", choices=sorted(KERNELS), default="bf16",
+                    help="the kernel --summarize-pmc summarises")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="time only the FP8 (e4m3) forward of the 128K last-rank shard and print its JSON")
     return ap.parse_args()
 
 
@@ -141,8 +158,12 @@ def cpu_baseline(spec, q, k, v, rows_n: int):
 
 
 def _timed(fn, stream, warmup: int, reps: int) -> float:
-    """Mean milliseconds of fn() over `reps` runs on `stream` (HIP events)."""
+    """Mean milliseconds of fn() over `reps` runs on `stream` (HIP events).
+    The inputs were made on the default stream, and the caching allocator
+    reuses memory in that stream's order only: everything queued so far must
+    finish before `stream` touches any of it."""
     import torch
+    torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -245,7 +266,73 @@ def secondary(seed: int, reps: int = 5):
                                   "over S=131072, causal, bf16; the two all-to-alls simulated by regrouping copies",
                       "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "regroup_bytes": regroup}
     del qs, ks, vs, os_, ws, lse
+    out["fp8"] = fp8_forward(cp, spec, seed, cs, xs, reps)
     return out
+
+
+def fp8_forward(cp, spec, seed: int, cs, xs, reps: int) -> dict:
+    """The causal 128K last-rank shard with e4m3 inputs: Q and the K/V blocks
+    quantised once on the device (per-(batch, head) scales), then the FP8 ring
+    forward with prefetch.  Seeded N(0, 1) inputs drawn on the device.  The
+    kernel rate is the algorithmic flops over the summed launch durations
+    (HIP events around each block launch), against the dense FP8 MFMA peak."""
+    import torch
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed + 404)
+    shape = (spec.B, spec.L, spec.H, spec.d)
+    desc = cp.Desc(spec.B, spec.H, spec.d, spec.N, spec.L, spec.rank, "bf16", "causal")
+    qd1 = cp.Desc(spec.B, spec.H, spec.d, 1, spec.L, 0, "bf16", "none")
+    codes, scales = [], []
+    x = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    for _ in range(1 + 2 * spec.N):
+        x.copy_(torch.randn(shape, generator=gen, device="cuda"))
+        c = torch.empty(shape, dtype=torch.uint8, device="cuda")
+        sc = torch.empty((spec.B, spec.H), device="cuda")
+        cp.cp_attn_quantize_fp8(qd1, x, c, sc)
+        codes.append(c)
+        scales.append(sc)
+    ms_q = _timed(lambda: cp.cp_attn_quantize_fp8(qd1, x, codes[-1], scales[-1], stream=cs), cs, 2, reps)
+    del x
+    qc, qs = codes[0], scales[0]
+    kc, ks = codes[1:1 + spec.N], scales[1:1 + spec.N]
+    vc, vs = codes[1 + spec.N:], scales[1 + spec.N:]
+    o = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((spec.B, spec.H, spec.L), device="cuda")
+    ws = cp.alloc_workspace(desc)
+    sched = cp.cp_attn_ring_schedule(desc, cp.CP_RING_PREFETCH)
+    prof = cp.Profiler(len(sched) * reps)
+
+    def run(p=None):
+        cp.cp_attn_rank_forward_fp8(desc, qc, qs, kc, ks, vc, vs, o, None, None, lse, workspace=ws,
+                                    compute_stream=cs, copy_stream=xs, flags=cp.CP_RING_PREFETCH, profiler=p)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    prof.reset()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(cs)
+    for _ in range(reps):
+        run(prof)
+    e1.record(cs)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    kms = prof.read()
+    prof.close()
+    assert torch.isfinite(o.float()).all(), "non-finite FP8 output"
+    fl = 4.0 * spec.d * spec.B * spec.H * cp.cp_attn_visible_pairs(desc)
+    k_tf = fl * reps / (sum(kms) * 1e-3) / 1e12
+    res = {"workload": "causal last-rank shard of the 128K example with e4m3 Q/K/V (per-(batch, head) scales), "
+                       "bf16 output: S=131072 N=4 L=32768 rank=3 B=1 H=32 d=128, ring prefetch",
+           "blocks": sched, "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+           "kernel_mean_ms": round(sum(kms) / max(1, len(kms)), 4), "kernel_tflops": round(k_tf, 2),
+           "frac_of_fp8_peak": round(k_tf / PEAK_FP8_TFLOPS, 4), "fp8_peak": PEAK_FP8_TFLOPS,
+           "traffic_bytes_per_launch": measured_traffic("fp8"),
+           "quantize_ms_per_block": round(ms_q, 4),
+           "quantize_gbs": round(spec.B * spec.L * spec.H * spec.d * 3 / (ms_q * 1e-3) / 1e9, 1),
+           "ring_bytes_copied": spec.B * spec.L * spec.H * spec.d * 2 * (len(sched) - 1)}
+    del codes, scales, o, lse, ws
+    return res
 
 
 def backward(spec, seed, desc, qd, kd, vd, out, lse, pairs, stream, reps: int = 3) -> dict:
@@ -281,8 +368,7 @@ def backward(spec, seed, desc, qd, kd, vd, out, lse, pairs, stream, reps: int = 
 def main():
     args = parse()
     if args.summarize_pmc:
-        blk = 32768 * 32 * 128 * 2          # one K or V block of the 128K example, bf16
-        print(json.dumps(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], blk, TRAFFIC_JSON)))
+        print(json.dumps(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.pmc_kernel)))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -294,6 +380,11 @@ def main():
     from harness.inputs import TENSOR_K, TENSOR_Q, TENSOR_V, bf16_bits, draw_shard, standard_configs
 
     cp.lib()
+    if args.fp8_only:
+        cs, xs = torch.cuda.Stream(), torch.cuda.Stream()
+        print(json.dumps(fp8_forward(cp, standard_configs(args.seed)[3], args.seed, cs, xs, max(args.steps, 1))),
+              flush=True)
+        return
     spec = standard_configs(args.seed)[3]
     N, L, H, d, r = spec.N, spec.L, spec.H, spec.d, spec.rank
     log(f"[bench] generating inputs for {spec.name}")

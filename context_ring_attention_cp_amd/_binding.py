@@ -34,6 +34,7 @@ EXPORTED = [
     "cp_attn_profiler_destroy", "cp_attn_status_string", "cp_attn_last_error",
     "cp_attn_bwd_delta", "cp_attn_block_backward", "cp_attn_rank_backward",
     "cp_attn_ulysses_workspace_bytes", "cp_attn_ulysses_forward", "cp_attn_quantize_fp8",
+    "cp_attn_rank_forward_fp8",
 ]
 
 
@@ -94,6 +95,9 @@ def lib() -> ctypes.CDLL:
         L.cp_attn_ulysses_forward.argtypes = [dp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                               ctypes.POINTER(vp), f32p, f32p, f32p, vp, ctypes.c_size_t, vp]
         L.cp_attn_quantize_fp8.argtypes = [dp, vp, vp, f32p, vp]
+        L.cp_attn_rank_forward_fp8.argtypes = [dp, vp, f32p, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                               ctypes.POINTER(vp), ctypes.POINTER(vp), vp, f32p, f32p, f32p, vp,
+                                               ctypes.c_size_t, vp, vp, i32, vp]
         L.cp_attn_status_string.argtypes = [i32]
         L.cp_attn_status_string.restype = ctypes.c_char_p
         L.cp_attn_last_error.argtypes = []
@@ -319,6 +323,37 @@ def cp_attn_quantize_fp8(desc: Desc, x, codes, scales, stream=None) -> None:
     if codes is None or scales is None:
         raise ValueError("codes and scales are required")
     _check(lib().cp_attn_quantize_fp8(desc.ref, _ptr(x), _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def cp_attn_rank_forward_fp8(desc: Desc, q, q_scale, k_blocks: Sequence, k_scales: Sequence, v_blocks: Sequence,
+                             v_scales: Sequence, out, m_out=None, l_out=None, lse_out=None, workspace=None,
+                             compute_stream=None, copy_stream=None, flags: int = CP_RING_PREFETCH,
+                             profiler: Optional["Profiler"] = None) -> None:
+    """q, k/v blocks: uint8 e4m3 codes [B, L, H, d]; scales float32 [B, H]; out bf16."""
+    import torch
+    c = desc.c
+    big, vec = _shapes(desc)
+    N = c.N
+    if not (len(k_blocks) == len(v_blocks) == len(k_scales) == len(v_scales) == N):
+        raise ValueError(f"need N={N} entries in k_blocks, k_scales, v_blocks and v_scales")
+    _check_tensor(q, "q", big, torch.uint8)
+    _check_tensor(q_scale, "q_scale", (c.B, c.H), torch.float32)
+    for t in list(k_blocks) + list(v_blocks):
+        _check_tensor(t, "k/v block", big, torch.uint8)
+    for t in list(k_scales) + list(v_scales):
+        _check_tensor(t, "k/v scale", (c.B, c.H), torch.float32)
+    _check_tensor(out, "out", big, torch.bfloat16)
+    for n, t in (("m_out", m_out), ("l_out", l_out), ("lse_out", lse_out)):
+        _check_tensor(t, n, vec, torch.float32)
+    if workspace is None or not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+        raise ValueError("workspace must be a device tensor")
+    arr = lambda ts: (ctypes.c_void_p * N)(*[_ptr(t) for t in ts])  # noqa: E731
+    cs = _stream(compute_stream)
+    xs = _stream(copy_stream) if copy_stream is not None else cs
+    _check(lib().cp_attn_rank_forward_fp8(desc.ref, _ptr(q), _ptr(q_scale), arr(k_blocks), arr(k_scales),
+                                          arr(v_blocks), arr(v_scales), _ptr(out), _ptr(m_out), _ptr(l_out),
+                                          _ptr(lse_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          cs, xs, int(flags), profiler.handle if profiler is not None else None))
 
 
 def cp_attn_bwd_delta(desc: Desc, o, d_o, delta, stream=None) -> None:

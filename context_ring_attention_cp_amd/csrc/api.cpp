@@ -500,13 +500,22 @@ cp_status cp_attn_rank_backward(const cp_attn_desc* desc, const void* q, const v
   return CP_OK;
 }
 
-cp_status cp_attn_rank_forward(const cp_attn_desc* desc, const void* q, const void* const* k_blocks,
-                               const void* const* v_blocks, void* out, float* m_out, float* l_out, float* lse_out,
-                               void* workspace, size_t workspace_bytes, void* compute_stream, void* copy_stream,
-                               int32_t flags, cp_attn_profiler* prof) {
+// The ring forward of one rank; with fp8 set, q and the blocks hold e4m3
+// codes with the given per-(b, h) scales and the output is bf16.
+static cp_status rank_forward_impl(const cp_attn_desc* desc, const void* q, const void* const* k_blocks,
+                                   const void* const* v_blocks, void* out, float* m_out, float* l_out, float* lse_out,
+                                   void* workspace, size_t workspace_bytes, void* compute_stream, void* copy_stream,
+                                   int32_t flags, cp_attn_profiler* prof, bool fp8, const float* q_scale,
+                                   const float* const* k_scales, const float* const* v_scales) {
   g_last_error.clear();
   cp_status st = check_desc(desc);
   if (st != CP_OK) return st;
+  if (fp8) {
+    if (desc->dtype != CP_BF16)
+      return fail(CP_ERR_UNSUPPORTED, "the FP8 forward writes a bf16 output: desc->dtype must be bf16 (dtype=%d)", desc->dtype);
+    if ((st = check_vec(q_scale, "q_scale", false)) != CP_OK) return st;
+    if (!k_scales || !v_scales) return fail(CP_ERR_INVALID_ARG, "k_scales/v_scales is NULL");
+  }
   if (flags & ~(CP_RING_PREFETCH | CP_RING_REVERSE)) return fail(CP_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   if ((st = check_tensor(q, "q")) != CP_OK || (st = check_tensor(out, "out")) != CP_OK ||
       (st = check_vec(m_out, "m_out", true)) != CP_OK || (st = check_vec(l_out, "l_out", true)) != CP_OK ||
@@ -516,6 +525,9 @@ cp_status cp_attn_rank_forward(const cp_attn_desc* desc, const void* q, const vo
   const std::vector<int32_t> sched = schedule(desc, flags);
   for (int32_t j : sched) {
     if ((st = check_tensor(k_blocks[j], "k_blocks[j]")) != CP_OK || (st = check_tensor(v_blocks[j], "v_blocks[j]")) != CP_OK)
+      return st;
+    if (fp8 && ((st = check_vec(k_scales[j], "k_scales[j]", false)) != CP_OK ||
+                (st = check_vec(v_scales[j], "v_scales[j]", false)) != CP_OK))
       return st;
   }
   const WorkspaceLayout wl = layout_of(desc);
@@ -531,7 +543,7 @@ cp_status cp_attn_rank_forward(const cp_attn_desc* desc, const void* q, const vo
   hipStream_t cs = (hipStream_t)compute_stream;
   hipStream_t xs = (hipStream_t)copy_stream;
   char* ws = (char*)workspace;
-  const size_t blk_bytes = (size_t)desc->B * desc->L * desc->H * desc->d * elt_bytes(desc->dtype);
+  const size_t blk_bytes = (size_t)desc->B * desc->L * desc->H * desc->d * (fp8 ? 1 : elt_bytes(desc->dtype));
   const int32_t nsteps = (int32_t)sched.size();
 
   // ready[t]: block of step t is in its slot; done[t]: step t's kernel finished with its slot
@@ -584,6 +596,11 @@ cp_status cp_attn_rank_forward(const cp_attn_desc* desc, const void* q, const vo
       if (e != hipSuccess) { cleanup(); return hip_fail(e, "ring receive"); }
     }
     BlockArgs a = block_args(desc, j, q, kp, vp);
+    if (fp8) {
+      a.q_scale = q_scale;
+      a.k_scale = k_scales[j];
+      a.v_scale = v_scales[j];
+    }
     const bool last = t == nsteps - 1;
     a.flags = (t > 0 ? F_READ_STATE : 0) | (last ? F_WRITE_FINAL : F_WRITE_STATE);
     a.st_o = (float*)(ws + wl.st_o);
@@ -595,7 +612,8 @@ cp_status cp_attn_rank_forward(const cp_attn_desc* desc, const void* q, const vo
     a.lse_out = lse_out;
     const bool timed = prof && prof->used < (int32_t)prof->start.size();
     if (timed && (e = hipEventRecord(prof->start[prof->used], cs)) != hipSuccess) { cleanup(); return hip_fail(e, "profiler record"); }
-    if ((e = launch_block(desc, a, cs)) != hipSuccess) { cleanup(); return hip_fail(e, "block kernel launch"); }
+    e = fp8 ? launch_block_fp8(a, desc->d, cs) : launch_block(desc, a, cs);
+    if (e != hipSuccess) { cleanup(); return hip_fail(e, "block kernel launch"); }
     if (timed) {
       if ((e = hipEventRecord(prof->stop[prof->used], cs)) != hipSuccess) { cleanup(); return hip_fail(e, "profiler record"); }
       prof->used++;
@@ -611,6 +629,24 @@ cp_status cp_attn_rank_forward(const cp_attn_desc* desc, const void* q, const vo
   }
   cleanup();
   return CP_OK;
+}
+
+cp_status cp_attn_rank_forward(const cp_attn_desc* desc, const void* q, const void* const* k_blocks,
+                               const void* const* v_blocks, void* out, float* m_out, float* l_out, float* lse_out,
+                               void* workspace, size_t workspace_bytes, void* compute_stream, void* copy_stream,
+                               int32_t flags, cp_attn_profiler* prof) {
+  return rank_forward_impl(desc, q, k_blocks, v_blocks, out, m_out, l_out, lse_out, workspace, workspace_bytes,
+                           compute_stream, copy_stream, flags, prof, false, nullptr, nullptr, nullptr);
+}
+
+cp_status cp_attn_rank_forward_fp8(const cp_attn_desc* desc, const void* q, const float* q_scale,
+                                   const void* const* k_blocks, const float* const* k_scales,
+                                   const void* const* v_blocks, const float* const* v_scales, void* out,
+                                   float* m_out, float* l_out, float* lse_out, void* workspace,
+                                   size_t workspace_bytes, void* compute_stream, void* copy_stream, int32_t flags,
+                                   cp_attn_profiler* prof) {
+  return rank_forward_impl(desc, q, k_blocks, v_blocks, out, m_out, l_out, lse_out, workspace, workspace_bytes,
+                           compute_stream, copy_stream, flags, prof, true, q_scale, k_scales, v_scales);
 }
 
 cp_status cp_attn_profiler_create(int32_t capacity, cp_attn_profiler** out) {

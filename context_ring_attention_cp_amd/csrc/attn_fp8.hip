@@ -1,0 +1,460 @@
+// FP8 (OCP e4m3) block kernel for gfx950: one rank's query shard against one
+// K/V block, Q, K and V given as e4m3 codes with one float32 scale per
+// (batch, head) each (value = decode(code) * scale), the output in bf16.
+//
+// The recurrence, work split, wave ping-pong, LDS ring, fetch schedule, masks
+// and lazy rescaling are those of the bf16 kernel (attn_mfma.hip); the online
+// softmax follows the compassingai.com context-parallelism page, section
+// "線上 Softmax".  That page also notes that the bytes CP moves depend on FP8
+// transfer (section "通訊量分析") and that FlashAttention-3 computes in FP8
+// (section "技術演進史").  What differs:
+//
+// Products on v_mfma_f32_32x32x64_f8f6f4 (both operands e4m3): A 32 x 64,
+// B 64 x 32, each lane holding 32 bytes (8 VGPRs).  The instruction pairs
+// byte e of lane half g of A with byte e of lane half g of B (one k each), and
+// its accumulator layout is the bf16 one: lane holds D[8(i/4) + 4g + i%4][r].
+//   S^T = K Q^T: A = K rows (through pi, as in bf16), bytes e of half g = head
+//     dims 64 s + 32 g + e; B = Q^T from registers with the same head dims.
+//     The two sub-tiles' accumulators hold keys 32 t + 16(i/8) + 8g + i%8.
+//   O^T += V^T P^T (64 keys, one MFMA per head-dim tile): byte e of half g
+//     stands for key 16(e/8) + 8g + e%8.  B = P^T is then simply the two S^T
+//     accumulators converted to e4m3 in order (bytes 0-15 from sub-tile 0,
+//     16-31 from sub-tile 1); A = V^T comes from four ds_read_b64_tr_b8 of the
+//     row-major V tile: within 16 lanes, lane s addresses row base + s/2 at
+//     column base + 8(s%2), and lane l receives column base + l of the 8 rows
+//     base .. base+7 (measured on the device with an index-filled LDS probe).
+// Scales: S = s_q s_k (codes product), folded into the exp2 coefficient; the
+//   accumulator holds sum P V_codes, so the running state is divided by s_v
+//   on load and O multiplied by s_v before it is stored.
+// P is rounded to e4m3 for the PV product (P <= 256 under the lazy rescale, so
+//   it never reaches the 448 limit); l sums the same rounded values, so O / l
+//   stays a convex combination of V rows.  The row sums come from the matrix
+//   core as well: one more MFMA per tile with an all-ones A operand
+//   (1.0 = code 0x38) and the same P^T operand leaves sum_k P[q][k] in every
+//   accumulator element of query q's lanes.  That MFMA falls in the compute
+//   phase, which is shorter than the softmax phase here, and saves the softmax
+//   the decode and the adds of 32 values per lane per tile.
+// Tiles are 64 keys x d bytes (8 KiB at d = 128), 4 stages, 64 KiB of LDS.
+#include "kernels.h"
+#include "gfx950_util.h"
+
+#include <math.h>
+
+namespace cpattn {
+namespace {
+
+using namespace dev;
+
+template <int V> struct Tag { static constexpr int value = V; };
+
+typedef int int8v __attribute__((ext_vector_type(8)));
+typedef int int2v __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int BM = 32 * kWaves;   // query rows per workgroup
+constexpr int BN = 64;            // keys per LDS tile
+constexpr int kStages = 4;        // LDS ring depth
+constexpr float kLazy = 8.0f;     // log2 headroom before a rescale
+
+// XOR swizzle of the 16-byte chunks of an e4m3 tile row of D bytes.  Operand
+// rows (16 lanes at rows pi(0..15), one chunk) and the 8-bit transpose loads
+// (8 consecutive rows x 2 consecutive chunks per 32 lanes) each touch 16
+// different 16-byte bank groups.
+template <int D> __device__ __forceinline__ int swz8(int row) {
+  if constexpr (D == 128) return (row >> 1) & 7;    // 2 rows per 256 bytes
+  else return (row >> 2) & 3;                       // 4 rows per 256 bytes
+}
+
+__device__ __forceinline__ floatx16 mfma8(const int8v& a, const int8v& b, const floatx16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
+  constexpr int CH = D / 16;         // 16-byte chunks per row
+  constexpr int NS = D / 64;         // k-steps of S^T = K Q^T
+  constexpr int NDT = D / 32;        // 32-row tiles of O^T
+  constexpr int NT = BN / 32;        // 32-key sub-tiles of S^T
+  constexpr int TILE = BN * D;       // bytes of one K or V tile
+  static_assert(NT == 2, "P^T operand built from two 32-key sub-tiles");
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages][2][TILE];   // [stage][K, V]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int r32 = lane & 31;
+  const int64_t L = a.L;
+  const int H = a.H;
+
+  const int nqt = (int)((L + BM - 1) / BM);
+  const int64_t nwg = (int64_t)nqt * H * a.B;
+  const int64_t bid = blockIdx.x;
+  const int64_t logical = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
+  const int64_t hb = logical / nqt;
+  const int qt = nqt - 1 - (int)(logical % nqt);
+  const int h = (int)(hb % H);
+  const int b = (int)(hb / H);
+
+  const int64_t rs = (int64_t)H * D;                        // row stride (bytes = elements)
+  const int64_t base = (int64_t)b * L * rs + (int64_t)h * D;
+  const uint8_t* __restrict__ qg = (const uint8_t*)a.q + base;
+  const uint8_t* __restrict__ kg = (const uint8_t*)a.k + base;
+  const uint8_t* __restrict__ vg = (const uint8_t*)a.v + base;
+  const int bh = b * H + h;
+  const float s_qk = a.q_scale[bh] * a.k_scale[bh];
+  const float s_v = a.v_scale[bh];
+
+  const int64_t q0 = (int64_t)qt * BM;
+  const int64_t qrow = q0 + 32 * w + r32;
+  const bool row_ok = qrow < L;
+  const int64_t p = a.q_pos0 + qrow;
+  const int mask = a.mask;
+  const bool doc = mask == MASK_DOC_CAUSAL;
+
+  const int nkt = (int)((L + BN - 1) / BN);
+  int kt_begin = 0, kt_end = nkt;
+  {
+    const int64_t wg_last = (q0 + BM < L ? q0 + BM : L) - 1;
+    if (mask != MASK_NONE) {
+      const int64_t hi = a.q_pos0 + wg_last - a.k_pos0;
+      kt_end = hi < 0 ? 0 : (int)(hi / BN + 1 < nkt ? hi / BN + 1 : nkt);
+      if (doc) {
+        const int64_t lo = doc_start_of(a.cu, a.ndocs, a.q_pos0 + q0) - a.k_pos0;
+        if (lo > 0) kt_begin = (int)(lo / BN < nkt ? lo / BN : nkt);
+      }
+    }
+  }
+  const bool rd = a.flags & F_READ_STATE;
+  if (kt_begin >= kt_end && rd && !(a.flags & (F_WRITE_FINAL | F_WRITE_PARTIAL))) return;
+
+  const int64_t w_first = q0 + 32 * w;
+  const bool wave_ok = w_first < L;
+  const int64_t w_last = (w_first + 31 < L ? w_first + 31 : L - 1);
+  const int64_t pw_first = a.q_pos0 + w_first, pw_last = a.q_pos0 + w_last;
+  int64_t ds_last = 0, dstart = 0;
+  if (doc && wave_ok) {
+    ds_last = doc_start_of(a.cu, a.ndocs, pw_last);
+    dstart = doc_start_of(a.cu, a.ndocs, row_ok ? p : pw_last);
+  }
+
+  // Q^T operand: head dims 64 s + 32 g .. +31 of this lane's query
+  int8v qreg[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (row_ok) {
+      const uint4 lo = *(const uint4*)(qg + qrow * rs + 64 * s + 32 * g);
+      const uint4 hi = *(const uint4*)(qg + qrow * rs + 64 * s + 32 * g + 16);
+      qreg[s] = int8v{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    } else {
+      qreg[s] = int8v{};
+    }
+  }
+
+  // Running state (base-2 units; the O accumulator in units of s_v; every
+  // element of lacc holds the row sum l of this lane's query).
+  floatx16 oacc[NDT];
+  floatx16 lacc = floatx16{};
+  float m_true = -INFINITY, m_ref = -INFINITY;
+  const int64_t st_row = ((int64_t)b * L + qrow) * ((int64_t)H * D) + (int64_t)h * D;
+  const int64_t ml_idx = ((int64_t)b * H + h) * L + qrow;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = floatx16{};
+  if (rd && row_ok) {
+    const float inv_v = 1.f / s_v;
+    m_true = m_ref = a.st_m[ml_idx] * kLog2e;
+    const float l0 = a.st_l[ml_idx];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lacc[i] = l0;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 v4 = *(const float4*)(a.st_o + st_row + 32 * dt + 8 * i4 + 4 * g);
+        oacc[dt][4 * i4 + 0] = v4.x * inv_v;
+        oacc[dt][4 * i4 + 1] = v4.y * inv_v;
+        oacc[dt][4 * i4 + 2] = v4.z * inv_v;
+        oacc[dt][4 * i4 + 3] = v4.w * inv_v;
+      }
+  }
+
+  const float c2 = a.scale_log2 * s_qk;
+
+  // Tile fetch by the 256 lanes of waves 0-3: fetch i of a lane fills 16-byte
+  // slot (i * 256 + tid) of the tile, row i * RPS + tid / CH, physical chunk
+  // tid % CH, holding logical chunk phys ^ swz8(row).  K and V share the
+  // swizzle, so one byte offset per lane serves both.
+  constexpr int kFetchThreads = kThreads / 2;
+  constexpr int DMA = BN * CH / kFetchThreads;
+  constexpr int RPS = kFetchThreads / CH;
+  static_assert(DMA >= 1 && (BN * CH) % kFetchThreads == 0 && RPS % 16 == 0, "tile fetch split");
+  const int f_tid = tid & (kFetchThreads - 1);
+  const int f_w = w & (kFetchThreads / 64 - 1);
+  const int f_row = f_tid / CH;
+  const int f_ph = f_tid % CH;
+  const uint32_t f_off = (uint32_t)((int64_t)f_row * rs + 16 * (f_ph ^ swz8<D>(f_row)));
+  const uint32_t smem_base = lds_addr(&smem[0][0][0]);
+  auto lds_of = [&](int st, int tensor, int byte) { return smem_base + (uint32_t)((st * 2 + tensor) * TILE + byte); };
+  auto fetch = [&](int kt, int st) {
+    const int64_t key0 = (int64_t)kt * BN;
+    if (key0 + BN <= L) {
+#pragma unroll
+      for (int i = 0; i < DMA; ++i) {
+        const int64_t rowoff = (key0 + i * RPS) * rs;
+        const int wbase = (i * kFetchThreads + 64 * f_w) * 16;
+        fetch16(kg + rowoff, f_off, lds_of(st, 0, wbase));
+        fetch16(vg + rowoff, f_off, lds_of(st, 1, wbase));
+      }
+    } else {
+      // the ragged last tile: offsets relative to its first row; rows past the
+      // end re-read row L-1 (finite data the mask drops)
+#pragma unroll
+      for (int i = 0; i < DMA; ++i) {
+        const int row = i * RPS + f_row;
+        const int64_t rrow = key0 + row < L ? row : L - 1 - key0;
+        const uint32_t off = (uint32_t)(rrow * rs + 16 * (f_ph ^ swz8<D>(f_row)));
+        const int wbase = (i * kFetchThreads + 64 * f_w) * 16;
+        fetch16(kg + key0 * rs, off, lds_of(st, 0, wbase));
+        fetch16(vg + key0 * rs, off, lds_of(st, 1, wbase));
+      }
+    }
+  };
+
+  // LDS operands.  K rows through pi (as in bf16): 32 bytes = logical chunks
+  // 4 s + 2 g and +1 of row 32 t + pi(r32).  V^T of head-dim tile dt: four
+  // 8-bit transpose loads, load x covering keys 8 (2x + g) .. +7.
+  const int krow_l = pi32(r32);
+  const int lam = lane & 15;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 8 * (lam & 1);   // + 32 dt
+  const int tr_row = lam >> 1;                                  // + 8 (2 x + g)
+  auto rd_k = [&](const uint8_t* __restrict__ Ks, int j) {     // j = s * NT + t
+    const int s = j / NT, t = j % NT;
+    const int row = 32 * t + krow_l;
+    const uint8_t* rp = Ks + row * D;
+    const uint4 lo = *(const uint4*)(rp + 16 * ((4 * s + 2 * g) ^ swz8<D>(row)));
+    const uint4 hi = *(const uint4*)(rp + 16 * ((4 * s + 2 * g + 1) ^ swz8<D>(row)));
+    return int8v{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  auto rd_v = [&](const uint8_t* __restrict__ Vs, int dt) {
+    const int col = 32 * dt + tr_col;
+    int2v x[4];
+#pragma unroll
+    for (int xx = 0; xx < 4; ++xx) {
+      const int row = 8 * (2 * xx + g) + tr_row;
+      x[xx] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) int2v*)(Vs + row * D + 16 * ((col >> 4) ^ swz8<D>(row)) + (col & 15)));
+    }
+    return int8v{x[0][0], x[0][1], x[1][0], x[1][1], x[2][0], x[2][1], x[3][0], x[3][1]};
+  };
+  // The compute phase as one stream of MFMAs (NQK of S^T = K Q^T, then NDT of
+  // O^T += V^T P^T and the row sums), each operand read RA MFMAs ahead in
+  // consumption order.
+  constexpr int NQK = NS * NT;
+  constexpr int RA = 3;
+  auto compute = [&](const uint8_t* __restrict__ Ks, const uint8_t* __restrict__ Vs, floatx16 (&sacc)[NT],
+                     const int8v& pb, auto qk_tag, auto pv_tag) {
+    constexpr bool QK = decltype(qk_tag)::value != 0, PV = decltype(pv_tag)::value != 0;
+    constexpr int J0 = QK ? 0 : NQK, J1 = PV ? NQK + NDT : NQK;
+    auto rd = [&](int j) { return j < NQK ? rd_k(Ks, j) : rd_v(Vs, j - NQK); };
+    if constexpr (QK) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) sacc[t] = floatx16{};
+    }
+    int8v ring[RA];
+#pragma unroll
+    for (int j = J0; j < J0 + RA && j < J1; ++j) ring[j - J0] = rd(j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = J0; j < J1; ++j) {
+      const int8v op = ring[(j - J0) % RA];
+      if (j < NQK) sacc[j % NT] = mfma8(op, qreg[j / NT], sacc[j % NT]);
+      else oacc[j - NQK] = mfma8(op, pb, oacc[j - NQK]);
+      if (j + RA < J1) ring[(j - J0) % RA] = rd(j + RA);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (PV) {
+      constexpr int kOne = 0x38383838;   // four e4m3 codes of 1.0
+      lacc = mfma8(int8v{kOne, kOne, kOne, kOne, kOne, kOne, kOne, kOne}, pb, lacc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Masks, row max and the lazy rescale: as in the bf16 kernel.
+  const int ragged_kt = (L % BN != 0) ? nkt - 1 : -1;
+  int causal_from = nkt, doc_below = 0;
+  if (mask != MASK_NONE) {
+    const int64_t x = pw_first - a.k_pos0 - (BN - 1);
+    causal_from = x < 0 ? 0 : (int)(x / BN + 1 < nkt ? x / BN + 1 : nkt);
+    if (doc) {
+      const int64_t y = ds_last - a.k_pos0;
+      doc_below = y <= 0 ? 0 : (int)((y + BN - 1) / BN < nkt ? (y + BN - 1) / BN : nkt);
+    }
+  }
+  auto need_mask = [&](int kt) -> bool { return kt == ragged_kt || kt >= causal_from || kt < doc_below; };
+  auto apply_mask = [&](int kt, floatx16 (&sacc)[NT]) {
+    const int64_t kbase = (int64_t)kt * BN;
+    const int64_t c_lo = a.k_pos0 + kbase;
+    int64_t hi64 = (L - kbase < BN ? L - kbase : BN) - 1;
+    if (mask != MASK_NONE && p - c_lo < hi64) hi64 = p - c_lo;
+    const int64_t lo64 = doc ? dstart - c_lo : 0;
+    const int hi = (int)(hi64 < -1 ? -1 : hi64) - 8 * g;
+    const int lo = (int)(lo64 < 0 ? 0 : (lo64 > BN ? BN : lo64)) - 8 * g;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int ko = 32 * t + 16 * (i >> 3) + (i & 7);
+        sacc[t][i] = (ko >= lo && ko <= hi) ? sacc[t][i] : -INFINITY;
+      }
+  };
+  auto row_max = [&](floatx16 (&sacc)[NT]) -> float {
+    float m0 = fmaxf(sacc[0][0], sacc[0][1]), m1 = fmaxf(sacc[0][2], sacc[0][3]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = (t == 0 ? 4 : 0); i < 16; i += 4) {
+        m0 = fmaxf(m0, fmaxf(sacc[t][i], sacc[t][i + 1]));
+        m1 = fmaxf(m1, fmaxf(sacc[t][i + 2], sacc[t][i + 3]));
+      }
+    const float mx = fmaxf(m0, m1);
+    return fmaxf(mx, xor32(mx));
+  };
+  auto rescale = [&](float mx) {
+    const float mt = mx * c2;
+    m_true = fmaxf(m_true, mt);
+    const bool need = mt > m_ref + kLazy;
+    if (__any(need)) {
+      const float nref = need ? m_true : m_ref;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - nref) : 1.f;
+      m_ref = nref;
+      lacc *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+    }
+  };
+  // P = exp2(x - m_ref), rounded to e4m3 as the PV B operand (bytes 0-15 from
+  // sub-tile 0, 16-31 from sub-tile 1).
+  auto exp_sum = [&](floatx16 (&sacc)[NT], int8v& pb) {
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][i], c2, -m_use));
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[t][4 * q], sacc[t][4 * q + 1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[t][4 * q + 2], sacc[t][4 * q + 3], word, true);
+        pb[4 * t + q] = word;
+      }
+  };
+
+  if (kt_begin < kt_end) {
+    const int grp = w >> 2;
+    auto stage = [&](int u) { return (u - kt_begin) & (kStages - 1); };
+    if (grp == 0) {
+      fetch(kt_begin, 0);
+      if (kt_begin + 1 < kt_end) fetch(kt_begin + 1, 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);              // vmcnt(0) lgkmcnt(0)
+    __syncthreads();
+    if (grp == 1) __syncthreads();                   // group 1 runs one phase behind
+    floatx16 sacc[NT];
+    int8v pb = int8v{};
+    auto step = [&](int u, auto qk_tag, auto pv_tag) {
+      constexpr bool QK = decltype(qk_tag)::value != 0;
+      compute(smem[stage(u)][0], smem[stage(u - 1)][1], sacc, pb, qk_tag, pv_tag);
+      lds_read_barrier();
+      const bool more = u + 2 < kt_end;
+      if (grp == 0 && more) {
+        fetch(u + 2, stage(u + 2));
+      }
+      if constexpr (QK) {
+        if (need_mask(u)) apply_mask(u, sacc);
+        rescale(row_max(sacc));
+        exp_sum(sacc, pb);
+      }
+      // tile u+1 must have landed: at most the fetch of tile u+2 (2 DMA tensors) outstanding
+      __asm__ volatile("" ::: "memory");
+      if (more) __builtin_amdgcn_s_waitcnt(0x0070 + 2 * DMA);   // vmcnt(2 DMA) lgkmcnt(0)
+      else __builtin_amdgcn_s_waitcnt(0x0070);
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+    };
+    step(kt_begin, Tag<1>{}, Tag<0>{});
+    for (int u = kt_begin + 1; u < kt_end; ++u) step(u, Tag<1>{}, Tag<1>{});
+    step(kt_end, Tag<0>{}, Tag<1>{});
+    if (grp == 0) __syncthreads();
+  }
+
+  // O back to true units, then to the true running max.
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= s_v;
+  if (m_true != -INFINITY && m_true != m_ref) {
+    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_true);
+    lacc *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+  }
+
+  if (!row_ok) return;
+  const float l_tot = lacc[0];
+  const bool has = l_tot > 0.f;
+  const float m_run = m_true;
+  // m in natural-log units of the true scores (c2 includes the FP8 scales)
+  if (a.flags & F_WRITE_STATE) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *(float4*)(a.st_o + st_row + 32 * dt + 8 * i4 + 4 * g) =
+            float4{oacc[dt][4 * i4], oacc[dt][4 * i4 + 1], oacc[dt][4 * i4 + 2], oacc[dt][4 * i4 + 3]};
+    if (g == 0) {
+      a.st_m[ml_idx] = m_run * kLn2;
+      a.st_l[ml_idx] = l_tot;
+    }
+  }
+  const float inv = has ? 1.f / l_tot : 0.f;
+  const float lse = has ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+  if (a.flags & F_WRITE_FINAL) {
+    bf16* outp = (bf16*)a.out + st_row;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const bf16x2 lo2 = __builtin_convertvector(float2v{oacc[dt][4 * i4] * inv, oacc[dt][4 * i4 + 1] * inv}, bf16x2);
+        const bf16x2 hi2 = __builtin_convertvector(float2v{oacc[dt][4 * i4 + 2] * inv, oacc[dt][4 * i4 + 3] * inv}, bf16x2);
+        *(bf16x4*)(outp + 32 * dt + 8 * i4 + 4 * g) = bf16x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+      }
+    if (g == 0) {
+      if (a.m_out) a.m_out[ml_idx] = m_run * kLn2;
+      if (a.l_out) a.l_out[ml_idx] = l_tot;
+      if (a.lse_out) a.lse_out[ml_idx] = lse;
+    }
+  }
+  if (a.flags & F_WRITE_PARTIAL) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *(float4*)(a.o_part + st_row + 32 * dt + 8 * i4 + 4 * g) =
+            float4{oacc[dt][4 * i4] * inv, oacc[dt][4 * i4 + 1] * inv, oacc[dt][4 * i4 + 2] * inv,
+                   oacc[dt][4 * i4 + 3] * inv};
+    if (g == 0) a.lse_part[ml_idx] = lse;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_block_fp8(const BlockArgs& a, int d, hipStream_t s) {
+  const int64_t nqt = (a.L + BM - 1) / BM;
+  const int64_t nwg = nqt * a.H * a.B;
+  if (d == 128) attn_block_fp8_kernel<128><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
+  else attn_block_fp8_kernel<64><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace cpattn

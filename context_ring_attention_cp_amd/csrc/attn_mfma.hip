@@ -213,13 +213,15 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
         fetch16(vg + rowoff, fv_off, lds_of(st, 1, wbase));
       }
     } else {
+      // the ragged last tile: byte offsets relative to its first row (32 bits suffice there)
+      const int64_t key0 = (int64_t)kt * BN;
 #pragma unroll
       for (int i = 0; i < DMA; ++i) {
-        int64_t key = (int64_t)kt * BN + i * RPS + f_row;
-        if (key > L - 1) key = L - 1;
+        const int row = i * RPS + f_row;
+        const int64_t rrow = key0 + row < L ? row : L - 1 - key0;
         const int wbase = (i * kFetchThreads + 64 * f_w) * 8;
-        fetch16(kg, (uint32_t)((key * rs + 8 * (f_ph ^ swz_k<D>(f_row))) * 2), lds_of(st, 0, wbase));
-        fetch16(vg, (uint32_t)((key * rs + 8 * (f_ph ^ swz_v<D>(f_row))) * 2), lds_of(st, 1, wbase));
+        fetch16(kg + key0 * rs, (uint32_t)((rrow * rs + 8 * (f_ph ^ swz_k<D>(f_row))) * 2), lds_of(st, 0, wbase));
+        fetch16(vg + key0 * rs, (uint32_t)((rrow * rs + 8 * (f_ph ^ swz_v<D>(f_row))) * 2), lds_of(st, 1, wbase));
       }
     }
   };

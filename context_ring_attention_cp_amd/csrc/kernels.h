@@ -42,6 +42,10 @@ struct BlockArgs {
   // partial outputs
   float* o_part;         // [B, L, H, d]
   float* lse_part;       // [B, H, L]
+  // FP8 (e4m3) inputs only: q, k, v hold codes; value = decode(code) * scale
+  const float* q_scale;  // [B, H] of the query shard
+  const float* k_scale;  // [B, H] of block j
+  const float* v_scale;  // [B, H] of block j
 };
 
 // Largest merge count handled by one kernel launch.
@@ -134,5 +138,7 @@ struct QuantArgs {
   int32_t B, H;
 };
 hipError_t launch_quantize_fp8(const QuantArgs& a, int d, hipStream_t s);
+// FP8 (e4m3) inputs, bf16 output; the same flags and state as the bf16 kernel.
+hipError_t launch_block_fp8(const BlockArgs& a, int d, hipStream_t s);
 
 }  // namespace cpattn

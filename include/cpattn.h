@@ -238,6 +238,24 @@ cp_status cp_attn_ulysses_forward(const cp_attn_desc* desc, const void* const* q
  * Errors: CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED (desc->dtype not bf16), CP_ERR_HIP. */
 cp_status cp_attn_quantize_fp8(const cp_attn_desc* desc, const void* x, void* codes, float* scales, void* stream);
 
+/* The whole forward of rank desc->rank over the simulated ring, as
+ * cp_attn_rank_forward, with FP8 inputs: q (device [B, L, H, d] e4m3 codes)
+ * with q_scale (device [B, H] float32), and per block j the codes k_blocks[j],
+ * v_blocks[j] with k_scales[j], v_scales[j] (HOST arrays of N device
+ * pointers; entries of blocks the rank never visits may be NULL), all as
+ * written by cp_attn_quantize_fp8.  The ring moves the one-byte codes (half
+ * the bytes of bf16).  Both products run on the FP8 matrix cores with float32
+ * accumulation; P is rounded to e4m3 for the P V product and l sums the same
+ * rounded values.  out is bf16 (desc->dtype must be CP_BF16); m, l, lse as in
+ * cp_attn_rank_forward; workspace of cp_attn_workspace_bytes(desc).
+ * Errors: CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED, CP_ERR_WORKSPACE, CP_ERR_HIP. */
+cp_status cp_attn_rank_forward_fp8(const cp_attn_desc* desc, const void* q, const float* q_scale,
+                                   const void* const* k_blocks, const float* const* k_scales,
+                                   const void* const* v_blocks, const float* const* v_scales, void* out,
+                                   float* m_out, float* l_out, float* lse_out, void* workspace,
+                                   size_t workspace_bytes, void* compute_stream, void* copy_stream, int32_t flags,
+                                   cp_attn_profiler* prof);
+
 /* ---- Backward of one rank shard ------------------------------------------
  * The backward walks the ring's K/V blocks again and recomputes what the
  * forward did not keep (compassingai.com page, section "反向傳播"; the Q, K, V

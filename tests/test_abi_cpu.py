@@ -370,3 +370,42 @@ def test_quantize_fp8_argument_errors():
         st = _status(lib.cp_attn_quantize_fp8, *args)
         assert st == status, (msg, st, B.last_error())
         assert msg in B.last_error(), (msg, B.last_error())
+
+
+def test_rank_forward_fp8_argument_errors():
+    lib = B.lib()
+    d = _desc()
+    P = ctypes.c_void_p
+    blocks = (P * 4)(FAKE, FAKE + 256, FAKE + 512, FAKE + 768)
+    scales = (P * 4)(FAKE + 1024, FAKE + 1280, FAKE + 1536, FAKE + 1792)
+    need = B.cp_attn_workspace_bytes(d)
+    S1, S2 = 0x1000, 0x2000
+
+    def call(desc=d, q=FAKE, qs=FAKE, kb=blocks, ks=scales, vb=blocks, vs=scales, out=FAKE, m=None, ws=FAKE,
+             nbytes=need, cs=S1, xs=S2, flags=1):
+        return _status(lib.cp_attn_rank_forward_fp8, desc.ref, q, qs, kb, ks, vb, vs, out, m, None, None, ws,
+                       nbytes, cs, xs, flags, None)
+
+    cases = [
+        (dict(desc=_desc(dtype="f32")), B.CP_ERR_UNSUPPORTED, "bf16"),
+        (dict(qs=None), B.CP_ERR_INVALID_ARG, "q_scale is NULL"),
+        (dict(qs=FAKE + 2), B.CP_ERR_INVALID_ARG, "q_scale"),
+        (dict(ks=None), B.CP_ERR_INVALID_ARG, "k_scales/v_scales is NULL"),
+        (dict(vs=None), B.CP_ERR_INVALID_ARG, "k_scales/v_scales is NULL"),
+        (dict(ks=(P * 4)(FAKE, None, FAKE, FAKE)), B.CP_ERR_INVALID_ARG, "k_scales[j]"),
+        (dict(vs=(P * 4)(FAKE, FAKE, FAKE + 2, FAKE)), B.CP_ERR_INVALID_ARG, "v_scales[j]"),
+        (dict(q=None), B.CP_ERR_INVALID_ARG, "q is NULL"),
+        (dict(flags=8), B.CP_ERR_INVALID_ARG, "flags"),
+        (dict(m=FAKE + 2), B.CP_ERR_INVALID_ARG, "m_out"),
+        (dict(nbytes=need - 1), B.CP_ERR_WORKSPACE, "needed"),
+        (dict(xs=S1), B.CP_ERR_INVALID_ARG, "copy_stream"),
+    ]
+    for kw, status, msg in cases:
+        st = call(**kw)
+        assert st == status, (msg, st, B.last_error())
+        assert msg in B.last_error(), (msg, B.last_error())
+    # scales of blocks a causal rank never visits may be NULL: rank 1 of 4 visits 1, 0 only
+    d1 = _desc(rank=1)
+    st = call(desc=d1, ks=(P * 4)(FAKE, FAKE, None, None), vs=(P * 4)(FAKE, FAKE, None, None),
+              kb=(P * 4)(FAKE, FAKE, None, None), vb=(P * 4)(FAKE, FAKE, None, None), nbytes=need - 1)
+    assert st == B.CP_ERR_WORKSPACE

@@ -5,13 +5,41 @@ float32 scale equals the oracle's, on ragged lengths (L not a multiple of
 the 256 rows a workgroup covers), both head dims, heads of very different
 magnitudes, an all-zero head, and a full-size 128K block (all scales, codes
 of sampled rows).
+
+The FP8 shard forward is compared with the oracle's float64 attention on the
+dequantised inputs (the oracle quantises the same bf16 draws itself).  Its
+tolerance follows from the arithmetic of the kernel:
+  * scores: products of two e4m3 values are exact in float32 and are summed
+    over at most 128 head dims in float32, so m (the row max) differs from the
+    oracle's only by float32 rounding, at most 128 * 2^-24 = 2^-17 of the sum
+    of the products' magnitudes, which stays below 8 |m| for the row max on
+    these inputs: max-abs 2e-3 + 2^-14 |m| (the bf16 path's 2e-3, plus the
+    term that matters for heads whose scores reach hundreds);
+  * P = exp(s - m_ref) is rounded to e4m3 before the P V product and l sums
+    the same rounded values.  A normal e4m3 value is within 2^-4 (half of the
+    3-bit mantissa's ulp) of its argument, relative; over a log-uniform
+    spread of P the rms relative error is 2^-4 / sqrt(3) * sqrt(0.541) =
+    0.0266.  Hence l: relative error at most 2^-4 plus the values below the
+    smallest normal (absolute error <= 2^-10 of the row max each, negligible
+    against l >= 1): bound 0.07; lse = m + log l: max-abs 0.07 plus m's bound;
+  * O = sum rho(p_k) v_k / sum rho(p_k): the error is
+    sum (rho(p_k) - p_k)(v_k - O) / sum rho(p_k), so over many elements its rms
+    is about 0.0266 of the rms of O itself: bound rms(err) <= 0.045 rms(O_ref).
+    A row with two keys of weights 1 and x errs at most
+    2^-4 x / (1 + x)^2 |v_1 - v_0| <= 2^-6 * 9 for |v| <= 4.5: max-abs 0.15;
+    mean-abs 1e-2.
+A mistake in the operand layouts (a key of P paired with the wrong V row, a
+head dim dropped, a scale missed) moves O by about its own size (relative rms
+near 1) and m or l far beyond these bounds.
 """
 import numpy as np
 import pytest
 
+import oracle
 import oracle.fp8 as F
-from harness.inputs import TENSOR_K, ShardSpec, draw_shard
-from tests.gpu_util import dev, say
+from harness.inputs import (TENSOR_K, TENSOR_Q, TENSOR_V, ShardSpec, draw_shard, make_inputs, round_to_bf16,
+                            standard_configs)
+from tests.gpu_util import dev, host, sample_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -44,7 +72,6 @@ def test_quantize_bit_exact(cp, d, L):
     x = rng.standard_normal((2, L, 4, d)).astype(np.float32) * np.array([1.0, 1e-3, 50.0, 1.0], np.float32)[None, None, :, None]
     x[1, :, 3, :] = 0.0                                   # one all-zero (b, h)
     x[0, 0, 0, :4] = [0.0, -0.0, 1e-30, -1e-30]           # zeros and values far below the smallest code
-    from harness.inputs import round_to_bf16
     x = round_to_bf16(x)
     say(f"[fp8 quantize] L={L} d={d}")
     codes, scales = _quantize_gpu(cp, x, d)
@@ -68,3 +95,199 @@ def test_quantize_full_size_block(cp):
     y = np.clip(x[:, rows] * inv[:, None, :, None], -448, 448).astype(np.float32)
     ref_codes = F.e4m3_encode(y)
     assert np.array_equal(codes[:, rows], ref_codes), "codes of sampled rows differ"
+
+
+# ----------------------------------------------------------------------------
+# the shard forward on e4m3 inputs
+
+FP8_TOL = dict(o_max=0.15, o_mean=1e-2, o_rel_rms=0.045, m_abs=2e-3, m_rel=2.0 ** -14, l_rel=0.07, lse_abs=0.07)
+
+
+def _codes_dev(q):
+    """oracle codes and scales -> device uint8 codes and float32 scales."""
+    return (torch.from_numpy(np.ascontiguousarray(q["codes"])).cuda(),
+            torch.from_numpy(np.ascontiguousarray(q["scale"], dtype=np.float32)).cuda())
+
+
+def _run_fp8(cp, spec, rank, qc, qs, kc, ks, vc, vs, flags):
+    cu_dev = None
+    if spec.mask == "doc_causal":
+        cu_dev = torch.from_numpy(np.asarray(spec.cu_seqlens, np.int32)).cuda()
+    d = cp.Desc(spec.B, spec.H, spec.d, spec.N, spec.L, rank, "bf16", spec.mask,
+                cu_seqlens=spec.cu_seqlens, cu_seqlens_dev=cu_dev)
+    big, vec = (spec.B, spec.L, spec.H, spec.d), (spec.B, spec.H, spec.L)
+    out = torch.full(big, float("nan"), dtype=torch.bfloat16, device="cuda")
+    m, l, lse = (torch.full(vec, float("nan"), device="cuda") for _ in range(3))
+    ws = cp.alloc_workspace(d)
+    cs, xs = torch.cuda.Stream(), torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        cp.cp_attn_rank_forward_fp8(d, qc, qs, kc, ks, vc, vs, out, m, l, lse, workspace=ws, compute_stream=cs,
+                                    copy_stream=xs, flags=flags)
+    cs.synchronize()
+    torch.cuda.synchronize()
+    return host(out), host(m), host(l), host(lse)
+
+
+def _check_fp8(got, ref, rows=None, heads=None):
+    o, m, l, lse = got
+    if rows is not None:
+        o = o[:, rows][:, :, heads]
+        m, l, lse = (x[:, heads][:, :, rows] for x in (m, l, lse))
+    t = FP8_TOL
+    r = ref["o"]
+    assert o.shape == r.shape and np.all(np.isfinite(o)), "o: shape or non-finite"
+    err = np.abs(o - r)
+    stats = {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
+             "rel_rms": float(np.sqrt(np.mean(err ** 2)) / max(np.sqrt(np.mean(r ** 2)), 1e-30))}
+    assert stats["max_abs"] <= t["o_max"], f"o: max-abs {stats}"
+    assert stats["mean_abs"] <= t["o_mean"], f"o: mean-abs {stats}"
+    assert stats["rel_rms"] <= t["o_rel_rms"], f"o: relative rms {stats}"
+    ninf = np.isneginf(ref["m"])
+    for name, g in (("m", m), ("l", l), ("lse", lse)):
+        assert np.array_equal(np.isneginf(g), np.isneginf(ref[name])), f"{name}: -inf pattern differs"
+    r_m = ref["m"][~ninf]
+    m_bound = t["m_abs"] + t["m_rel"] * np.abs(r_m)
+    stats["m"] = float(np.max(np.abs(m[~ninf] - r_m) / m_bound, initial=0.0))     # fraction of the bound
+    assert stats["m"] <= 1.0, f"m: {stats}"
+    stats["l"] = float(np.max(np.abs(l[~ninf] / ref["l"][~ninf] - 1), initial=0.0))
+    assert stats["l"] <= t["l_rel"], f"l: {stats}"
+    stats["lse"] = float(np.max(np.abs(lse[~ninf] - ref["lse"][~ninf]) / (t["lse_abs"] + m_bound), initial=0.0))
+    assert stats["lse"] <= 1.0, f"lse: {stats}"
+    return stats
+
+
+def _quantized_inputs(spec, seed, ranks):
+    inp = make_inputs(spec, seed=seed, ranks=ranks)
+    qz = {r: F.quantize_heads(inp["q"][r]) for r in ranks}
+    kz = [F.quantize_heads(inp["k"][j]) for j in range(spec.N)]
+    vz = [F.quantize_heads(inp["v"][j]) for j in range(spec.N)]
+    return qz, kz, vz
+
+
+def _oracle_fp8(spec, rank, qz, kz, vz, rows=None, heads=None):
+    return F.fp8_rank_attention(qz["codes"], qz["scale"], [z["codes"] for z in kz], [z["scale"] for z in kz],
+                                [z["codes"] for z in vz], [z["scale"] for z in vz], rank, spec.N, spec.mask,
+                                spec.cu_seqlens, rows=rows, heads=heads)
+
+
+def _small_cu(S):
+    pts, x = [0], 0
+    for n in (37, 130, 5, 300, 64, 1, 211, 90, 400):
+        x += n
+        if x >= S:
+            break
+        pts.append(x)
+    return np.asarray(pts + [S], np.int32)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", ["none", "causal", "doc_causal"])
+def test_fp8_forward_small_every_rank(cp, d, mask):
+    """N = 3 shards of L = 300 (several 256-row query tiles and 64-key tiles,
+    ragged tails), B = 2, H = 2: every rank, every output element."""
+    N, L, H, B = 3, 300, 2, 2
+    spec = ShardSpec(S=N * L, N=N, H=H, d=d, dtype="bf16", mask=mask, B=B, cfg_id=111,
+                     cu_seqlens=_small_cu(N * L) if mask == "doc_causal" else None)
+    qz, kz, vz = _quantized_inputs(spec, 2, range(N))
+    kd = [_codes_dev(z) for z in kz]
+    vd = [_codes_dev(z) for z in vz]
+    for r in range(N):
+        say(f"[fp8 fwd small] d={d} mask={mask} rank={r}")
+        qc, qs = _codes_dev(qz[r])
+        got = _run_fp8(cp, spec, r, qc, qs, [x[0] for x in kd], [x[1] for x in kd], [x[0] for x in vd],
+                       [x[1] for x in vd], cp.CP_RING_PREFETCH)
+        stats = _check_fp8(got, _oracle_fp8(spec, r, qz[r], kz, vz))
+        say(f"   {stats}")
+
+
+@pytest.mark.parametrize("flags", ["serial", "reverse"])
+def test_fp8_forward_ring_variants(cp, flags):
+    """Copies on the compute stream, and the reversed ring order: same bound."""
+    N, L = 4, 200
+    spec = ShardSpec(S=N * L, N=N, H=3, d=128, dtype="bf16", mask="causal", cfg_id=112)
+    qz, kz, vz = _quantized_inputs(spec, 3, [N - 1])
+    kd = [_codes_dev(z) for z in kz]
+    vd = [_codes_dev(z) for z in vz]
+    qc, qs = _codes_dev(qz[N - 1])
+    fl = 0 if flags == "serial" else cp.CP_RING_PREFETCH | cp.CP_RING_REVERSE
+    say(f"[fp8 fwd ring] flags={flags}")
+    got = _run_fp8(cp, spec, N - 1, qc, qs, [x[0] for x in kd], [x[1] for x in kd], [x[0] for x in vd],
+                   [x[1] for x in vd], fl)
+    _check_fp8(got, _oracle_fp8(spec, N - 1, qz[N - 1], kz, vz))
+
+
+@pytest.mark.parametrize("L", [1, 65])
+def test_fp8_forward_degenerate(cp, L):
+    """One-token and 65-token shards, heads of very different magnitudes and
+    an all-zero query head (scale 1, codes 0: uniform weights over the
+    visible keys)."""
+    N, H = 2, 4
+    spec = ShardSpec(S=N * L, N=N, H=H, d=64, dtype="bf16", mask="causal", cfg_id=113)
+    inp = make_inputs(spec, seed=4, ranks=range(N))
+    mag_q = np.array([1.0, 1e-3, 20.0, 1.0], np.float32)[None, None, :, None]
+    mag_k = np.array([1.0, 20.0, 20.0, 1.0], np.float32)[None, None, :, None]   # head 2: scores of std 400
+    for r in range(N):
+        inp["q"][r] = round_to_bf16(inp["q"][r] * mag_q)
+        inp["q"][r][:, :, 3, :] = 0.0
+    for j in range(N):
+        inp["k"][j] = round_to_bf16(inp["k"][j] * mag_k)
+    qz = {r: F.quantize_heads(inp["q"][r]) for r in range(N)}
+    kz = [F.quantize_heads(inp["k"][j]) for j in range(N)]
+    vz = [F.quantize_heads(inp["v"][j]) for j in range(N)]
+    kd = [_codes_dev(z) for z in kz]
+    vd = [_codes_dev(z) for z in vz]
+    for r in range(N):
+        say(f"[fp8 fwd degenerate] L={L} rank={r}")
+        qc, qs = _codes_dev(qz[r])
+        got = _run_fp8(cp, spec, r, qc, qs, [x[0] for x in kd], [x[1] for x in kd], [x[0] for x in vd],
+                       [x[1] for x in vd], cp.CP_RING_PREFETCH)
+        _check_fp8(got, _oracle_fp8(spec, r, qz[r], kz, vz))
+
+
+def _quantize_dev(cp, x_dev, spec):
+    desc = cp.Desc(spec.B, spec.H, spec.d, 1, spec.L, 0, "bf16", "none")
+    codes = torch.empty(x_dev.shape, dtype=torch.uint8, device="cuda")
+    scales = torch.empty((spec.B, spec.H), device="cuda")
+    cp.cp_attn_quantize_fp8(desc, x_dev, codes, scales)
+    return codes, scales
+
+
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_fp8_forward_full_size(cp, cfg):
+    """The causal 128K last-rank shard and the packed-document shard at full
+    size: bf16 draws quantised on the device (codes checked bit-exact against
+    the oracle's on the sampled heads), the FP8 ring forward with prefetch,
+    sampled rows of three heads against the oracle."""
+    spec = standard_configs(seed=0)[cfg]
+    blocks = oracle.ring_schedule(spec.N, spec.rank, spec.L, spec.mask, spec.cu_seqlens)
+    heads = sorted({0, spec.H - 1, int(np.random.default_rng(cfg + 17).integers(spec.H))})
+    say(f"[fp8 full cfg {cfg}] {spec.name}: blocks {blocks}, heads {heads}")
+    q = draw_shard(spec, 0, TENSOR_Q, spec.rank)
+    qc, qs = _quantize_dev(cp, dev(q, "bf16"), spec)
+    qz = F.quantize_heads(q[:, :, heads])
+    assert np.array_equal(qc.cpu().numpy()[:, :, heads], qz["codes"])
+    del q
+    kc, ks, vc, vs = ([None] * spec.N for _ in range(4))
+    kz, vz = [None] * spec.N, [None] * spec.N
+    for j in blocks:
+        for tid, cs_, ss_, zz in ((TENSOR_K, kc, ks, kz), (TENSOR_V, vc, vs, vz)):
+            x = draw_shard(spec, 0, tid, j)
+            cs_[j], ss_[j] = _quantize_dev(cp, dev(x, "bf16"), spec)
+            zz[j] = F.quantize_heads(x[:, :, heads])
+            del x
+            assert np.array_equal(cs_[j].cpu().numpy()[:, :, heads], zz[j]["codes"]), f"codes of block {j}"
+    got = _run_fp8(cp, spec, spec.rank, qc, qs, kc, ks, vc, vs, cp.CP_RING_PREFETCH)
+    extra = []
+    if spec.cu_seqlens is not None:
+        s0 = spec.rank * spec.L
+        extra = [x - s0 + e for x in spec.cu_seqlens if s0 <= x < s0 + spec.L for e in (-1, 0, 1)]
+    rows = sample_rows(spec.L, cfg, extra=extra)
+    ref = F.fp8_rank_attention(qz["codes"], qz["scale"], [z["codes"] if z else None for z in kz],
+                               [z["scale"] if z else None for z in kz], [z["codes"] if z else None for z in vz],
+                               [z["scale"] if z else None for z in vz], spec.rank, spec.N, spec.mask,
+                               spec.cu_seqlens, rows=rows)
+    stats = _check_fp8(got, ref, rows=rows, heads=heads)
+    say(f"[fp8 full cfg {cfg}] {len(rows)} rows x {len(heads)} heads: {stats}")
+    for arr in got:
+        assert np.all(np.isfinite(arr))
