@@ -16,13 +16,14 @@
 //   S^T = K Q^T: A = K rows (through pi, as in bf16), bytes e of half g = head
 //     dims 64 s + 32 g + e; B = Q^T from registers with the same head dims.
 //     The two sub-tiles' accumulators hold keys 32 t + 16(i/8) + 8g + i%8.
-//   O^T += V^T P^T (64 keys, one MFMA per head-dim tile): byte e of half g
-//     stands for key 16(e/8) + 8g + e%8.  B = P^T is then simply the two S^T
-//     accumulators converted to e4m3 in order (bytes 0-15 from sub-tile 0,
-//     16-31 from sub-tile 1); A = V^T comes from four ds_read_b64_tr_b8 of the
-//     row-major V tile: within 16 lanes, lane s addresses row base + s/2 at
-//     column base + 8(s%2), and lane l receives column base + l of the 8 rows
-//     base .. base+7 (measured on the device with an index-filled LDS probe).
+//   O^T += V^T P^T (64 keys per MFMA, one per head-dim tile and key half):
+//     byte e of half g stands for key 16(e/8) + 8g + e%8 of the 64-key half.
+//     B = P^T is then simply two S^T accumulators converted to e4m3 in order
+//     (bytes 0-15 from sub-tile 2h, 16-31 from sub-tile 2h+1); A = V^T comes
+//     from four ds_read_b64_tr_b8 of the row-major V tile: within 16 lanes,
+//     lane s addresses row base + s/2 at column base + 8(s%2), and lane l
+//     receives column base + l of the 8 rows base .. base+7 (measured on the
+//     device with an index-filled LDS probe).
 // Scales: S = s_q s_k (codes product), folded into the exp2 coefficient; the
 //   accumulator holds sum P V_codes, so the running state is divided by s_v
 //   on load and O multiplied by s_v before it is stored.
@@ -30,11 +31,15 @@
 //   it never reaches the 448 limit); l sums the same rounded values, so O / l
 //   stays a convex combination of V rows.  The row sums come from the matrix
 //   core as well: one more MFMA per tile with an all-ones A operand
-//   (1.0 = code 0x38) and the same P^T operand leaves sum_k P[q][k] in every
+//   (1.0 = code 0x38) and a P^T operand leaves sum_k P[q][k] in every
 //   accumulator element of query q's lanes.  That MFMA falls in the compute
 //   phase, which is shorter than the softmax phase here, and saves the softmax
 //   the decode and the adds of 32 values per lane per tile.
-// Tiles are 64 keys x d bytes (8 KiB at d = 128), 4 stages, 64 KiB of LDS.
+// Tiles are 128 keys x d bytes (16 KiB at d = 128), 4 stages, 128 KiB of LDS:
+//   with FP8 products a 64-key tile is too little work per phase to carry the
+//   phase's fixed costs (barriers, waits, the row max exchange); 128-key tiles
+//   were 5 % faster on the same device.  The operands are read 2 MFMAs ahead,
+//   which keeps the kernel within 256 VGPRs.
 #include "kernels.h"
 #include "gfx950_util.h"
 
@@ -53,7 +58,7 @@ typedef int int2v __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int BM = 32 * kWaves;   // query rows per workgroup
-constexpr int BN = 64;            // keys per LDS tile
+constexpr int BN = 128;           // keys per LDS tile
 constexpr int kStages = 4;        // LDS ring depth
 constexpr float kLazy = 8.0f;     // log2 headroom before a rescale
 
@@ -76,8 +81,9 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
   constexpr int NS = D / 64;         // k-steps of S^T = K Q^T
   constexpr int NDT = D / 32;        // 32-row tiles of O^T
   constexpr int NT = BN / 32;        // 32-key sub-tiles of S^T
+  constexpr int NH = BN / 64;        // 64-key halves: one P^T operand each (two sub-tiles)
   constexpr int TILE = BN * D;       // bytes of one K or V tile
-  static_assert(NT == 2, "P^T operand built from two 32-key sub-tiles");
+  static_assert(NT == 2 * NH, "P^T operands built from pairs of 32-key sub-tiles");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages][2][TILE];   // [stage][K, V]
 
@@ -237,27 +243,27 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
     const uint4 hi = *(const uint4*)(rp + 16 * ((4 * s + 2 * g + 1) ^ swz8<D>(row)));
     return int8v{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
-  auto rd_v = [&](const uint8_t* __restrict__ Vs, int dt) {
+  auto rd_v = [&](const uint8_t* __restrict__ Vs, int kh, int dt) {
     const int col = 32 * dt + tr_col;
     int2v x[4];
 #pragma unroll
     for (int xx = 0; xx < 4; ++xx) {
-      const int row = 8 * (2 * xx + g) + tr_row;
+      const int row = 64 * kh + 8 * (2 * xx + g) + tr_row;
       x[xx] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
           (__attribute__((address_space(3))) int2v*)(Vs + row * D + 16 * ((col >> 4) ^ swz8<D>(row)) + (col & 15)));
     }
     return int8v{x[0][0], x[0][1], x[1][0], x[1][1], x[2][0], x[2][1], x[3][0], x[3][1]};
   };
-  // The compute phase as one stream of MFMAs (NQK of S^T = K Q^T, then NDT of
-  // O^T += V^T P^T and the row sums), each operand read RA MFMAs ahead in
-  // consumption order.
+  // The compute phase as one stream of MFMAs (NQK of S^T = K Q^T, then NH NDT
+  // of O^T += V^T P^T and NH of the row sums), each operand read RA MFMAs
+  // ahead in consumption order.
   constexpr int NQK = NS * NT;
-  constexpr int RA = 3;
+  constexpr int RA = 2;
   auto compute = [&](const uint8_t* __restrict__ Ks, const uint8_t* __restrict__ Vs, floatx16 (&sacc)[NT],
-                     const int8v& pb, auto qk_tag, auto pv_tag) {
+                     const int8v (&pb)[NH], auto qk_tag, auto pv_tag) {
     constexpr bool QK = decltype(qk_tag)::value != 0, PV = decltype(pv_tag)::value != 0;
-    constexpr int J0 = QK ? 0 : NQK, J1 = PV ? NQK + NDT : NQK;
-    auto rd = [&](int j) { return j < NQK ? rd_k(Ks, j) : rd_v(Vs, j - NQK); };
+    constexpr int J0 = QK ? 0 : NQK, J1 = PV ? NQK + NH * NDT : NQK;
+    auto rd = [&](int j) { return j < NQK ? rd_k(Ks, j) : rd_v(Vs, (j - NQK) / NDT, (j - NQK) % NDT); };
     if constexpr (QK) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) sacc[t] = floatx16{};
@@ -270,14 +276,17 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
     for (int j = J0; j < J1; ++j) {
       const int8v op = ring[(j - J0) % RA];
       if (j < NQK) sacc[j % NT] = mfma8(op, qreg[j / NT], sacc[j % NT]);
-      else oacc[j - NQK] = mfma8(op, pb, oacc[j - NQK]);
+      else oacc[(j - NQK) % NDT] = mfma8(op, pb[(j - NQK) / NDT], oacc[(j - NQK) % NDT]);
       if (j + RA < J1) ring[(j - J0) % RA] = rd(j + RA);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (PV) {
       constexpr int kOne = 0x38383838;   // four e4m3 codes of 1.0
-      lacc = mfma8(int8v{kOne, kOne, kOne, kOne, kOne, kOne, kOne, kOne}, pb, lacc);
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kh = 0; kh < NH; ++kh) {
+        lacc = mfma8(int8v{kOne, kOne, kOne, kOne, kOne, kOne, kOne, kOne}, pb[kh], lacc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
@@ -334,9 +343,9 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
       for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
     }
   };
-  // P = exp2(x - m_ref), rounded to e4m3 as the PV B operand (bytes 0-15 from
-  // sub-tile 0, 16-31 from sub-tile 1).
-  auto exp_sum = [&](floatx16 (&sacc)[NT], int8v& pb) {
+  // P = exp2(x - m_ref), rounded to e4m3 as the PV B operands (operand h:
+  // bytes 0-15 from sub-tile 2h, 16-31 from sub-tile 2h+1).
+  auto exp_sum = [&](floatx16 (&sacc)[NT], int8v (&pb)[NH]) {
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -348,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
       for (int q = 0; q < 4; ++q) {
         int word = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[t][4 * q], sacc[t][4 * q + 1], 0, false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[t][4 * q + 2], sacc[t][4 * q + 3], word, true);
-        pb[4 * t + q] = word;
+        pb[t / 2][4 * (t % 2) + q] = word;
       }
   };
 
@@ -363,7 +372,9 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
     __syncthreads();
     if (grp == 1) __syncthreads();                   // group 1 runs one phase behind
     floatx16 sacc[NT];
-    int8v pb = int8v{};
+    int8v pb[NH];
+#pragma unroll
+    for (int kh = 0; kh < NH; ++kh) pb[kh] = int8v{};
     auto step = [&](int u, auto qk_tag, auto pv_tag) {
       constexpr bool QK = decltype(qk_tag)::value != 0;
       compute(smem[stage(u)][0], smem[stage(u - 1)][1], sacc, pb, qk_tag, pv_tag);
