@@ -68,11 +68,12 @@ def _pmc_rows(d: str, counter: str):
     return sorted(rows)
 
 
-def summarize_pmc(fetch_dir: str, write_dir: str, which: str = "bf16") -> dict:
+def summarize_pmc(fetch_dir: str, write_dir: str, which: str = "bf16", out: str = None) -> dict:
     """HBM traffic of an attention kernel from a FETCH_SIZE run and a
     WRITE_SIZE run (KiB per dispatch) of its one-step bench command.  Each
     counter is scaled by what it reads for the ring-receive copy kernels of
-    the same run, which move one K or V block each."""
+    the same run, which move one K or V block each.  Written to the kernel's
+    committed summary under profiles/ unless `out` names another file."""
     kern = KERNELS[which]
     copy_bytes, attn_kernel = kern["copy_bytes"], kern["name"]
     res = {}
@@ -92,7 +93,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, which: str = "bf16") -> dict:
                "fetch": res["fetch"], "write": res["write"], "calibration_copy_bytes": copy_bytes,
                "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o <name> -- "
                           + kern["cmd"]}
-    with open(os.path.join(ROOT, "profiles", kern["json"]), "w") as f:
+    with open(out or os.path.join(ROOT, "profiles", kern["json"]), "w") as f:
         json.dump(summary, f, indent=1)
     return summary
 
@@ -152,7 +153,7 @@ def cpu_baseline(spec, q, k, v, rows_n: int):
     pairs = int(np.sum(p + 1)) if spec.mask == "causal" else int(rows_n * spec.S)
     flops = 4.0 * spec.d * pairs
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"{rows_n} evenly spaced query rows of head 0 of 32 ({pairs} visible pairs, "
+            "sample": f"{rows_n} evenly spaced query rows of head 0 of {spec.H} ({pairs} visible pairs, "
                       f"{dt:.1f} s wall, fp64 numpy, materialised score rows)",
             "host_cpus": len(os.sched_getaffinity(0))}
 
