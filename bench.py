@@ -179,19 +179,21 @@ def _timed(fn, stream, warmup: int, reps: int) -> float:
 
 def _timed_flushed(fn, stream, warmup: int, reps: int, flush) -> dict:
     """Per-iteration HIP-event times of fn() on `stream`, each iteration
-    preceded (outside its events) by a write of the 512 MiB `flush` buffer on
+    preceded (outside its events) by a read of the 512 MiB `flush` buffer on
     the same stream, which evicts the L2 and the 256 MB Infinity Cache, so that
-    inputs that would fit there are read from HBM as in a real ring step.
-    Returns the median and the mean in ms."""
+    inputs that would fit there are read from HBM as in a real ring step.  A
+    read leaves clean lines behind (a write would leave the timed kernel to
+    write back up to the whole cache).  Returns the median and the mean in ms."""
     import torch
     torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    sink = torch.zeros(2, device="cuda")
     ev = []
     for i in range(reps):
         with torch.cuda.stream(stream):
-            flush.fill_(float(i))
+            sink[i % 2] = flush.sum()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         fn()
@@ -221,7 +223,7 @@ def secondary(seed: int, reps: int = 5):
     out = {}
     cfgs = standard_configs(seed)
     cs, xs = torch.cuda.Stream(), torch.cuda.Stream()
-    flush = torch.empty(128 << 20, device="cuda")        # 512 MiB, written between iterations of cfg 2 and 4
+    flush = torch.ones(128 << 20, device="cuda")         # 512 MiB, read between iterations of cfg 2 and 4
     for cfg in (2, 5):
         spec = cfgs[cfg]
         cu_dev = None if spec.cu_seqlens is None else torch.from_numpy(spec.cu_seqlens).to("cuda")

@@ -6,9 +6,12 @@
 // terms summed in the caller's order.
 // finalize: out = O / l, lse = m + ln l (same section, last line).
 //
-// Both are streaming kernels: each thread owns 4 consecutive head-dim
-// elements of one (batch, row, head), so a wave reads/writes whole 512-byte
-// rows of float32 with 16-byte accesses.
+// Both are streaming kernels: each thread owns 8 (merge) or 4 (finalize)
+// consecutive head-dim elements of one (batch, row, head), so a wave
+// reads/writes whole 512-byte rows of float32 with 16-byte accesses.  A workgroup covers consecutive rows
+// of one (batch, head) (grid: row chunks x B*H), so its lse loads are
+// contiguous and a thread finds its row and column with shifts and one
+// 32-bit division per workgroup index rather than 64-bit divisions.
 #include "kernels.h"
 
 #include <math.h>
@@ -41,18 +44,21 @@ constexpr int kRegParts = 16;
 // Partials loaded back to back before their multiply-adds.
 constexpr int kBatch = 8;
 
+// grid: x = chunk of kThreads / (D / 8) rows, y = b * H + h.  Each thread
+// owns 8 consecutive head-dim elements (two 16-byte loads per part), so a
+// thread keeps 2 kBatch partial loads in flight.
+template <int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
-  const int d4 = a.d / 4;
-  const int64_t total = (int64_t)a.B * a.L * a.H * d4;
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= total) return;
-  const int x4 = (int)(idx % d4);
-  const int64_t rowhead = idx / d4;               // (b * L + row) * H + h
-  const int h = (int)(rowhead % a.H);
-  const int64_t br = rowhead / a.H;               // b * L + row
-  const int64_t row = br % a.L;
-  const int b = (int)(br / a.L);
-  const int64_t ml = ((int64_t)b * a.H + h) * a.L + row;
+  constexpr int D8 = D / 8;                       // threads per row
+  constexpr int RPW = kThreads / D8;              // rows per workgroup
+  const int bh = blockIdx.y;
+  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+  const int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / D8;
+  if (row >= a.L) return;
+  const int x8 = threadIdx.x % D8;
+  const int64_t rowhead = ((int64_t)b * a.L + row) * a.H + h;
+  const int64_t ml = (int64_t)bh * a.L + row;
+  const int64_t off = rowhead * D + 8 * x8;
   const int n = a.n;
 
   // lse = ln sum exp(lse_j), in base 2 with the max factored out
@@ -64,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     mx = fmaxf(mx, l2[j]);
   }
   for (int j = kRegParts; j < n; ++j) mx = fmaxf(mx, a.lse[j][ml] * kLog2e);
-  float4 o = float4{0.f, 0.f, 0.f, 0.f};
+  float4 o0 = float4{0.f, 0.f, 0.f, 0.f}, o1 = o0;
   float lse = -INFINITY;
   if (mx != -INFINITY) {
     float tot = 0.f;
@@ -73,15 +79,15 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     for (int j = kRegParts; j < n; ++j) tot += __builtin_amdgcn_exp2f(__builtin_fmaf(a.lse[j][ml], kLog2e, -mx));
     const float lse2 = mx + __builtin_amdgcn_logf(tot);   // v_log_f32 is log2
     lse = lse2 * kLn2;
-    const int64_t off = rowhead * a.d + 4 * x4;
-    // terms in the given order, kBatch partial loads in flight at a time
+    // terms in the given order, 2 kBatch partial loads in flight at a time
     for (int j0 = 0; j0 < n; j0 += kBatch) {
-      float4 v[kBatch];
+      float4 v0[kBatch], v1[kBatch];
       float wj[kBatch];
 #pragma unroll
       for (int t = 0; t < kBatch; ++t) {
         const int j = j0 + t;
-        v[t] = j < n ? *(const float4*)(a.o[j] + off) : float4{0.f, 0.f, 0.f, 0.f};
+        v0[t] = j < n ? *(const float4*)(a.o[j] + off) : float4{0.f, 0.f, 0.f, 0.f};
+        v1[t] = j < n ? *(const float4*)(a.o[j] + off + 4) : float4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int t = 0; t < kBatch; ++t) {
@@ -91,35 +97,39 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
       }
 #pragma unroll
       for (int t = 0; t < kBatch; ++t) {
-        o.x = __builtin_fmaf(wj[t], v[t].x, o.x);
-        o.y = __builtin_fmaf(wj[t], v[t].y, o.y);
-        o.z = __builtin_fmaf(wj[t], v[t].z, o.z);
-        o.w = __builtin_fmaf(wj[t], v[t].w, o.w);
+        o0.x = __builtin_fmaf(wj[t], v0[t].x, o0.x);
+        o0.y = __builtin_fmaf(wj[t], v0[t].y, o0.y);
+        o0.z = __builtin_fmaf(wj[t], v0[t].z, o0.z);
+        o0.w = __builtin_fmaf(wj[t], v0[t].w, o0.w);
+        o1.x = __builtin_fmaf(wj[t], v1[t].x, o1.x);
+        o1.y = __builtin_fmaf(wj[t], v1[t].y, o1.y);
+        o1.z = __builtin_fmaf(wj[t], v1[t].z, o1.z);
+        o1.w = __builtin_fmaf(wj[t], v1[t].w, o1.w);
       }
     }
   }
-  store4(a.out, rowhead * a.d + 4 * x4, a.out_bf16, o);
-  if (x4 == 0 && a.lse_out) a.lse_out[ml] = lse;
+  store4(a.out, off, a.out_bf16, o0);
+  store4(a.out, off + 4, a.out_bf16, o1);
+  if (x8 == 0 && a.lse_out) a.lse_out[ml] = lse;
 }
 
+template <int D>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalizeArgs a) {
-  const int d4 = a.d / 4;
-  const int64_t total = (int64_t)a.B * a.L * a.H * d4;
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= total) return;
-  const int x4 = (int)(idx % d4);
-  const int64_t rowhead = idx / d4;
-  const int h = (int)(rowhead % a.H);
-  const int64_t br = rowhead / a.H;
-  const int64_t row = br % a.L;
-  const int b = (int)(br / a.L);
-  const int64_t ml = ((int64_t)b * a.H + h) * a.L + row;
+  constexpr int D4 = D / 4;
+  constexpr int RPW = kThreads / D4;
+  const int bh = blockIdx.y;
+  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+  const int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / D4;
+  if (row >= a.L) return;
+  const int x4 = threadIdx.x % D4;
+  const int64_t rowhead = ((int64_t)b * a.L + row) * a.H + h;
+  const int64_t ml = (int64_t)bh * a.L + row;
   const float l = a.st_l[ml];
   const float m = a.st_m[ml];
   const bool has = l > 0.f;
   const float inv = has ? 1.f / l : 0.f;
-  const float4 v = *(const float4*)(a.st_o + rowhead * a.d + 4 * x4);
-  store4(a.out, rowhead * a.d + 4 * x4, a.out_bf16, float4{v.x * inv, v.y * inv, v.z * inv, v.w * inv});
+  const float4 v = *(const float4*)(a.st_o + rowhead * D + 4 * x4);
+  store4(a.out, rowhead * D + 4 * x4, a.out_bf16, float4{v.x * inv, v.y * inv, v.z * inv, v.w * inv});
   if (x4 == 0) {
     if (a.m_out) a.m_out[ml] = m;
     if (a.l_out) a.l_out[ml] = l;
@@ -129,15 +139,20 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalizeArgs a) {
 
 }  // namespace
 
+// B * H <= 65535 (the grid's y extent) is checked by the caller.
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
-  const int64_t total = (int64_t)a.B * a.L * a.H * (a.d / 4);
-  merge_kernel<<<dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(a);
+  const int rpw = kThreads / (a.d / 8);
+  const dim3 grid((unsigned)((a.L + rpw - 1) / rpw), (unsigned)(a.B * a.H));
+  if (a.d == 128) merge_kernel<128><<<grid, dim3(kThreads), 0, s>>>(a);
+  else merge_kernel<64><<<grid, dim3(kThreads), 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s) {
-  const int64_t total = (int64_t)a.B * a.L * a.H * (a.d / 4);
-  finalize_kernel<<<dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0, s>>>(a);
+  const int rpw = kThreads / (a.d / 4);
+  const dim3 grid((unsigned)((a.L + rpw - 1) / rpw), (unsigned)(a.B * a.H));
+  if (a.d == 128) finalize_kernel<128><<<grid, dim3(kThreads), 0, s>>>(a);
+  else finalize_kernel<64><<<grid, dim3(kThreads), 0, s>>>(a);
   return hipGetLastError();
 }
 
