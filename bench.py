@@ -413,7 +413,7 @@ def main():
         print(json.dumps(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.pmc_kernel)))
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py runs on one GPU only: this library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -57,7 +57,7 @@ extern "C" {
 typedef enum {
   CP_OK = 0,
   CP_ERR_INVALID_ARG = 1,   /* a null/misaligned pointer, bad shape, bad index, malformed cu_seqlens */
-  CP_ERR_UNSUPPORTED = 2,   /* a valid request this build does not implement (e.g. d not in {64,128}) */
+  CP_ERR_UNSUPPORTED = 2,   /* a valid request this library does not implement (e.g. d not in {64,128}) */
   CP_ERR_WORKSPACE = 3,     /* workspace missing or smaller than cp_attn_workspace_bytes() */
   CP_ERR_HIP = 4            /* a HIP runtime call failed; the message names it */
 } cp_status;

@@ -33,7 +33,7 @@ What it computes (all in float64):
   wangyu.me page, sections "Ring Attention" and "通信模式").
 * ``brute_force`` - pure-Python loops with math.exp / math.fsum for tiny inputs.
 
-Readings of points the pages leave open (each also listed in the design doc):
+Readings of points the pages leave open:
   * causal visibility includes the diagonal: key c is visible to query p iff
     c <= p (the pages say a token sees the tokens before it; without the
     diagonal the first row of rank 0 would see nothing);

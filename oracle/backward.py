@@ -29,7 +29,7 @@ written out:
   the shard and the shard's contributions to dK_j, dV_j of each block
   (zero for blocks it does not see).
 
-Readings (each also listed in the design doc):
+Readings of points the pages leave open:
   * the backward of a rank shard returns that rank's dQ and its contributions
     to every block's dK, dV; summing the contributions of all ranks gives the
     gradient of the full-sequence attention (the ring carries them home);

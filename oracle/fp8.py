@@ -10,7 +10,7 @@ What the pages fix: the compassingai.com context-parallelism page notes that
 the bytes CP moves depend on whether the exchanged blocks are compressed or
 sent in FP8 (section "通訊量分析"), and that FlashAttention-3 computes
 attention in FP8 (section "技術演進史").  They fix no format or scaling; the
-readings below are this build's (each also listed in the design doc):
+readings below are this library's choices:
 
 * format: OCP FP8 E4M3 (1 sign bit, 4 exponent bits with bias 7, 3 mantissa
   bits, largest finite value 448, no infinities), the format of the

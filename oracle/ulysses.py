@@ -29,7 +29,7 @@ Functions:
   step 2 taken from the definition (``attention.attention_rows``: masked
   softmax over materialised score rows).
 
-Readings (each also listed in the design doc):
+Readings of points the pages leave open:
   * rank r takes the contiguous head group [r H/N, (r+1) H/N); H must be a
     multiple of N;
   * after the first all-to-all the sequence is the ranks' shards in rank
