@@ -318,16 +318,20 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
         sacc[t][i] = (ko >= lo && ko <= hi) ? sacc[t][i] : -INFINITY;
       }
   };
+  // Four independent chains, each folding two new values per step (v_max3).
   auto row_max = [&](floatx16 (&sacc)[NT]) -> float {
-    float m0 = fmaxf(sacc[0][0], sacc[0][1]), m1 = fmaxf(sacc[0][2], sacc[0][3]);
+    float m[4];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int c = 0; c < 4; ++c) m[c] = sacc[0][c];
 #pragma unroll
-      for (int i = (t == 0 ? 4 : 0); i < 16; i += 4) {
-        m0 = fmaxf(m0, fmaxf(sacc[t][i], sacc[t][i + 1]));
-        m1 = fmaxf(m1, fmaxf(sacc[t][i + 2], sacc[t][i + 3]));
+    for (int k = 4; k < 16 * NT; k += 8)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int i0 = k + 2 * c, i1 = i0 + 1;
+        if (i1 < 16 * NT) m[c] = fmaxf(fmaxf(m[c], sacc[i0 / 16][i0 % 16]), sacc[i1 / 16][i1 % 16]);
+        else if (i0 < 16 * NT) m[c] = fmaxf(m[c], sacc[i0 / 16][i0 % 16]);
       }
-    const float mx = fmaxf(m0, m1);
+    const float mx = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
     return fmaxf(mx, xor32(mx));
   };
   auto rescale = [&](float mx) {
