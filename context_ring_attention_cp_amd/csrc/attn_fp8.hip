@@ -359,7 +359,12 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[t][4 * q], sacc[t][4 * q + 1], 0, false);
+        // The first conversion keeps bytes 2-3 of its third operand, which the
+        // second one overwrites.  Passing the previous tile's word (already
+        // consumed by the P V products of this step's compute phase) keeps the
+        // conversions in place in the operand registers.
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[t][4 * q], sacc[t][4 * q + 1], pb[t / 2][4 * (t % 2) + q],
+                                                   false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[t][4 * q + 2], sacc[t][4 * q + 3], word, true);
         pb[t / 2][4 * (t % 2) + q] = word;
       }
