@@ -384,3 +384,40 @@ def test_profiler_records_each_attention_launch(cp):
     prof.reset()
     assert prof.read() == []
     prof.close()
+
+
+@pytest.mark.parametrize("N,d,mask", [(24, 64, "none"), (64, 128, "doc_causal")])
+def test_many_parts_and_long_ring(cp, N, d, mask):
+    """Rings of 24 and of CP_MAX_RING = 64 blocks of 16 tokens (every tile
+    ragged): the PARTIAL_LSE partials of all blocks merged in a seeded shuffled
+    order (more parts than the merge keeps in registers; under the document
+    mask most parts are empty), and the prefetching rank forward over the whole
+    ring, both against the oracle."""
+    L, H = 16, 2
+    spec = ShardSpec(S=N * L, N=N, H=H, d=d, dtype="bf16", mask=mask, cfg_id=108,
+                     cu_seqlens=_small_cu(N * L) if mask == "doc_causal" else None)
+    r = N // 2
+    inp = make_inputs(spec, seed=9, ranks=[r])
+    cu_dev = None
+    if mask == "doc_causal":
+        cu_dev = torch.from_numpy(np.asarray(spec.cu_seqlens, np.int32)).cuda()
+    desc = _desc(cp, spec, r, cu_dev)
+    q = dev(inp["q"][r], "bf16")
+    kb, vb = _blocks(spec, inp)
+    big, vec = (1, L, H, d), (1, H, L)
+    ops = [torch.full(big, float("nan"), device="cuda") for _ in range(N)]
+    lps = [torch.full(vec, float("nan"), device="cuda") for _ in range(N)]
+    say(f"[long ring] N={N} d={d} mask={mask}: {N} partials")
+    for j in range(N):
+        cp.cp_attn_block_partial(desc, j, cp.CP_MODE_PARTIAL_LSE, q, kb[j], vb[j], o_part=ops[j], lse_part=lps[j])
+    order = [int(x) for x in np.random.default_rng(N).permutation(N)]
+    out = torch.full(big, float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full(vec, float("nan"), device="cuda")
+    cp.cp_attn_merge_lse(desc, ops, lps, order, out, lse)
+    torch.cuda.synchronize()
+    ref = oracle.rank_attention(inp["q"][r], inp["k"], inp["v"], r, N, mask, spec.cu_seqlens)
+    check_o(host(out), ref["o"], "bf16")
+    check_stat(host(lse), ref["lse"], "bf16", "lse")
+    say(f"[long ring] N={N}: rank forward")
+    got = run_rank(cp, spec, r, q, kb, vb, cp.CP_RING_PREFETCH)
+    _check_all(got, ref, "bf16")
