@@ -36,7 +36,9 @@ _BLK = 32768 * 32 * 128                 # elements of one K or V block of the 12
 # from, the committed PMC summary, the bytes of one ring-receive copy of the
 # same run (the counters' calibration) and the command the runs profile.
 KERNELS = {
-    "bf16": dict(name="attn_block_bf16_kernel<128>", srcs=("attn_mfma.hip", "gfx950_util.h", "kernels.h"),
+    # the bf16 kernel's two forms (<128, false>: V row-major, the rank's own
+    # block; <128, true>: V in the tiles the ring receive writes) share the prefix
+    "bf16": dict(name="attn_block_bf16_kernel<128", srcs=("attn_mfma.hip", "gfx950_util.h", "kernels.h"),
                  json="attn_block_bf16__causal_128k_last_rank.traffic.json", copy_bytes=2 * _BLK,
                  cmd="python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-secondary"),
     "fp8": dict(name="attn_block_fp8_kernel<128>", srcs=("attn_fp8.hip", "gfx950_util.h", "kernels.h"),

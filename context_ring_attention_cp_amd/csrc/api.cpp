@@ -165,6 +165,8 @@ struct WorkspaceLayout {
 WorkspaceLayout layout_of(const cp_attn_desc* d) {
   WorkspaceLayout w;
   const size_t blk = round_up((size_t)d->B * d->L * d->H * d->d * elt_bytes(d->dtype), 256);
+  // a bf16 V slot holds the tiled copy, whose keys are padded to whole 64-key tiles
+  const size_t blk_v = round_up((size_t)d->B * v_tiled_keys(d->L) * d->H * d->d * elt_bytes(d->dtype), 256);
   const size_t ost = round_up((size_t)d->B * d->L * d->H * d->d * 4, 256);
   const size_t vec = round_up((size_t)d->B * d->H * d->L * 4, 256);
   size_t off = 0;
@@ -172,7 +174,7 @@ WorkspaceLayout layout_of(const cp_attn_desc* d) {
     w.slot_k[s] = off;
     off += blk;
     w.slot_v[s] = off;
-    off += blk;
+    off += blk_v;
   }
   w.st_o = off;
   off += ost;
@@ -549,6 +551,10 @@ static cp_status rank_forward_impl(const cp_attn_desc* desc, const void* q, cons
   char* ws = (char*)workspace;
   const size_t blk_bytes = (size_t)desc->B * desc->L * desc->H * desc->d * (fp8 ? 1 : elt_bytes(desc->dtype));
   const int32_t nsteps = (int32_t)sched.size();
+  // bf16 V blocks are received in head-dim-major 64-key tiles (the receive
+  // writes that layout; the attention kernel fetches each tile as one
+  // contiguous run and reads V^T operands as whole 16-byte rows)
+  const bool v_tiled = !fp8 && desc->dtype == CP_BF16;
 
   // ready[t]: block of step t is in its slot; done[t]: step t's kernel finished with its slot
   std::vector<hipEvent_t> ready(nsteps, nullptr), done(nsteps, nullptr);
@@ -571,8 +577,9 @@ static cp_status rank_forward_impl(const cp_attn_desc* desc, const void* q, cons
   auto enqueue_copy = [&](int32_t t, hipStream_t s) -> hipError_t {
     const int32_t j = sched[t];
     hipError_t r = hipMemcpyAsync(slot_k(t), k_blocks[j], blk_bytes, hipMemcpyDeviceToDevice, s);
-    if (r == hipSuccess) r = hipMemcpyAsync(slot_v(t), v_blocks[j], blk_bytes, hipMemcpyDeviceToDevice, s);
-    return r;
+    if (r != hipSuccess) return r;
+    if (v_tiled) return launch_v_tiles(v_blocks[j], slot_v(t), desc->L, desc->B, desc->H, desc->d, s);
+    return hipMemcpyAsync(slot_v(t), v_blocks[j], blk_bytes, hipMemcpyDeviceToDevice, s);
   };
   // the copy stream starts after everything already queued on the compute stream (inputs ready)
   hipEvent_t start_ev = nullptr;
@@ -606,7 +613,8 @@ static cp_status rank_forward_impl(const cp_attn_desc* desc, const void* q, cons
       a.v_scale = v_scales[j];
     }
     const bool last = t == nsteps - 1;
-    a.flags = (t > 0 ? F_READ_STATE : 0) | (last ? F_WRITE_FINAL : F_WRITE_STATE);
+    a.flags = (t > 0 ? F_READ_STATE : 0) | (last ? F_WRITE_FINAL : F_WRITE_STATE) |
+              (t > 0 && v_tiled ? F_V_TILED : 0);
     a.st_o = (float*)(ws + wl.st_o);
     a.st_m = (float*)(ws + wl.st_m);
     a.st_l = (float*)(ws + wl.st_l);

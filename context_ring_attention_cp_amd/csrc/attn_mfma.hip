@@ -36,6 +36,12 @@
 // receives the elements at column base + lam of rows base .. base+3 -
 // 4 consecutive keys of one head-dim column.
 //
+// Tiled V (F_V_TILED, the layout the ring's receive writes): V arrives as
+// [B, H, T, d, 64] (T tiles of 64 keys, each head-dim-major, zero past L), so
+// a key tile of V^T is one contiguous run, fetched whole, and the A operand of
+// O^T = V^T P^T (8 consecutive keys of one head-dim row) is one 16-byte LDS
+// read per lane instead of two transpose loads.
+//
 // Overlap: the two waves of a SIMD belong to two groups that alternate MFMA
 // phases and softmax phases one phase apart (see the main loop).
 //
@@ -64,7 +70,7 @@ constexpr int BN = 64;            // keys per LDS tile
 constexpr int kStages = 4;        // LDS ring depth
 constexpr float kLazy = 8.0f;     // log2 headroom before a rescale
 
-template <int D>
+template <int D, bool VT>
 __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) {
   constexpr int CH = D / 8;          // 16-byte chunks per row
   constexpr int NS = D / 16;         // k-steps of S^T = K Q^T
@@ -102,7 +108,8 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   const int64_t base = (int64_t)b * L * rs + (int64_t)h * D;
   const bf16* __restrict__ qg = (const bf16*)a.q + base;
   const bf16* __restrict__ kg = (const bf16*)a.k + base;
-  const bf16* __restrict__ vg = (const bf16*)a.v + base;
+  // tiled V: this head's tiles of D x BN elements, one after another
+  const bf16* __restrict__ vg = (const bf16*)a.v + (VT ? ((int64_t)b * H + h) * D * v_tiled_keys(L) : base);
 
   const int64_t q0 = (int64_t)qt * BM;
   const int64_t qrow = q0 + 32 * w + r32;                   // this lane's query row
@@ -203,6 +210,17 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   // are uniform, so the fetch destinations are scalar arithmetic.
   const uint32_t smem_base = lds_addr(&smem[0][0][0]);
   auto lds_of = [&](int st, int tensor, int e) { return smem_base + (uint32_t)(((st * 2 + tensor) * TILE + e) * 2); };
+  // Tiled V: a V^T tile is D rows of BN keys (128 bytes, CHT chunks), stored
+  // contiguously.  Fetch i of a lane fills V^T row i * RPST + f_tid / CHT,
+  // physical chunk f_tid % CHT, with the swizzle of 128-byte rows (row bits
+  // 1-3, below RPST).  Keys past L are zeros in the block itself, so every
+  // tile is read whole.
+  constexpr int CHT = BN / 8;
+  constexpr int RPST = kFetchThreads / CHT;
+  static_assert(D * CHT == BN * CH && RPST % 16 == 0, "tiled V fetch split");
+  const int ft_row = f_tid / CHT;
+  const uint32_t fvt_off = (uint32_t)((ft_row * BN + 8 * ((f_tid % CHT) ^ swz_k<BN>(ft_row))) * 2);
+  auto fetch_vt = [&](int kt, int i, uint32_t lds) { fetch16(vg + ((int64_t)kt * D + i * RPST) * BN, fvt_off, lds); };
   auto fetch = [&](int kt, int st) {
     if ((int64_t)(kt + 1) * BN <= L) {
 #pragma unroll
@@ -210,7 +228,8 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
         const int64_t rowoff = ((int64_t)kt * BN + i * RPS) * rs;          // uniform
         const int wbase = (i * kFetchThreads + 64 * f_w) * 8;
         fetch16(kg + rowoff, fk_off, lds_of(st, 0, wbase));
-        fetch16(vg + rowoff, fv_off, lds_of(st, 1, wbase));
+        if constexpr (VT) fetch_vt(kt, i, lds_of(st, 1, wbase));
+        else fetch16(vg + rowoff, fv_off, lds_of(st, 1, wbase));
       }
     } else {
       // the ragged last tile: byte offsets relative to its first row (32 bits suffice there)
@@ -221,7 +240,8 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
         const int64_t rrow = key0 + row < L ? row : L - 1 - key0;
         const int wbase = (i * kFetchThreads + 64 * f_w) * 8;
         fetch16(kg + key0 * rs, (uint32_t)((rrow * rs + 8 * (f_ph ^ swz_k<D>(f_row))) * 2), lds_of(st, 0, wbase));
-        fetch16(vg + key0 * rs, (uint32_t)((rrow * rs + 8 * (f_ph ^ swz_v<D>(f_row))) * 2), lds_of(st, 1, wbase));
+        if constexpr (VT) fetch_vt(kt, i, lds_of(st, 1, wbase));
+        else fetch16(vg + key0 * rs, (uint32_t)((rrow * rs + 8 * (f_ph ^ swz_v<D>(f_row))) * 2), lds_of(st, 1, wbase));
       }
     }
   };
@@ -244,6 +264,11 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
     return *(const bf16x8*)(Ks + row * D + 8 * ((2 * (j / NT) + g) ^ swz_k<D>(row)));
   };
   auto rd_v = [&](const bf16* __restrict__ Vs, int k) {
+    if constexpr (VT) {
+      // row 32 dt + r32 of V^T (a head dim), keys 16 kstep + 8 g .. + 7: logical chunk 2 kstep + g
+      const int row = 32 * (k % NDT) + r32;
+      return *(const bf16x8*)(Vs + row * BN + 8 * ((2 * (k / NDT) + g) ^ swz_k<BN>(row)));
+    }
     const int col = 32 * (k % NDT) + tr_col;
     const int row0 = 16 * (k / NDT) + 8 * g + tr_row;
     const int row1 = row0 + 4;
@@ -486,8 +511,14 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
 hipError_t launch_block_bf16(const BlockArgs& a, int d, hipStream_t s) {
   const int64_t nqt = (a.L + BM - 1) / BM;
   const int64_t nwg = nqt * a.H * a.B;
-  if (d == 128) attn_block_bf16_kernel<128><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
-  else attn_block_bf16_kernel<64><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
+  const bool vt = (a.flags & F_V_TILED) != 0;
+  if (d == 128) {
+    if (vt) attn_block_bf16_kernel<128, true><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
+    else attn_block_bf16_kernel<128, false><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
+  } else {
+    if (vt) attn_block_bf16_kernel<64, true><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
+    else attn_block_bf16_kernel<64, false><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

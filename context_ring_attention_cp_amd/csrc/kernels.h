@@ -12,7 +12,11 @@ enum : int32_t {
   F_WRITE_STATE = 2,    // store the running state
   F_WRITE_FINAL = 4,    // store out = O / l (input dtype) and m, l, lse
   F_WRITE_PARTIAL = 8,  // store normalised O (float32) and lse of this block alone
+  F_V_TILED = 16,       // bf16 only: v in head-dim-major 64-key tiles [B, H, T, d, 64], zero past L
 };
+
+// Keys of a tiled V block: L rounded up to whole 64-key tiles (T = that / 64).
+__host__ __device__ inline int64_t v_tiled_keys(int64_t L) { return (L + 63) / 64 * 64; }
 
 enum : int32_t { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_DOC_CAUSAL = 2 };
 
@@ -20,7 +24,7 @@ enum : int32_t { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_DOC_CAUSAL = 2 };
 struct BlockArgs {
   const void* q;         // [B, L, H, d]
   const void* k;         // [B, L, H, d] block j
-  const void* v;         // [B, L, H, d] block j
+  const void* v;         // [B, L, H, d] block j (F_V_TILED: [B, H, T, d, 64])
   int64_t L;             // shard length (rows of q, rows of k/v)
   int32_t B, H;
   int64_t q_pos0;        // global position of query row 0 (rank * L)
@@ -108,6 +112,9 @@ struct DeltaArgs {
 // Launchers return the hipError_t of the launch.
 hipError_t launch_block_bf16(const BlockArgs& a, int d, hipStream_t s);
 hipError_t launch_block_f32(const BlockArgs& a, int d, hipStream_t s);
+// bf16 V block [B, L, H, d] -> the tiled layout F_V_TILED reads, keys L..
+// filled with zeros.
+hipError_t launch_v_tiles(const void* v, void* v_tiled, int64_t L, int32_t B, int32_t H, int d, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
 hipError_t launch_bwd_delta(const DeltaArgs& a, int d, hipStream_t s);

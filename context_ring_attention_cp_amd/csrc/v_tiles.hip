@@ -1,0 +1,67 @@
+// Tiled copy of a bf16 V block, written by the simulated ring receive:
+// [B, L, H, d] -> [B, H, T, d, 64] with T = ceil(L / 64) tiles of 64 keys,
+// each tile head-dim-major (d rows of 64 consecutive keys), zeros for keys
+// from L on.  A key tile of V^T is then one contiguous run (16 KiB at
+// d = 128) that the attention kernel fetches into LDS as it is, and the A
+// operand of O^T = V^T P^T (8 consecutive keys of one head dim) is one 16-byte
+// LDS read per lane.  In a real ring the owner of a block would write this
+// layout once and the block would travel in it; here the layout change is
+// fused into the receive copy.  HBM-bound: 2 d bytes read and written per key
+// and head.
+#include "kernels.h"
+#include "gfx950_util.h"
+
+namespace cpattn {
+namespace {
+
+using namespace dev;
+
+constexpr int kTile = 64;        // keys per workgroup
+constexpr int kThreadsT = 256;
+
+// One workgroup per (batch, head, 64-key tile): the tile's 64 rows of d
+// elements go through LDS (rows padded by 16 bytes), then every lane writes
+// 16-byte runs of 8 consecutive keys of one head-dim row.
+template <int D>
+__global__ __launch_bounds__(kThreadsT) void v_tiles_kernel(const bf16* __restrict__ v, bf16* __restrict__ vt,
+                                                           int64_t L, int H) {
+  constexpr int CH = D / 8;                 // 16-byte chunks of a key row
+  constexpr int RS = D + 8;                 // padded LDS row (elements)
+  __shared__ __attribute__((aligned(16))) bf16 t[kTile * RS];
+  const int64_t ntile = v_tiled_keys(L) / kTile;
+  const int64_t bid = blockIdx.x;
+  const int64_t kt = bid % ntile;
+  const int64_t hb = bid / ntile;
+  const int h = (int)(hb % H);
+  const int64_t b = hb / H;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int s = tid; s < kTile * CH; s += kThreadsT) {
+    const int r = s / CH, c = s % CH;
+    const int64_t key = kt * kTile + r;
+    bf16x8 x = {};
+    if (key < L) x = *(const bf16x8*)(v + ((b * L + key) * H + h) * D + 8 * c);
+    *(bf16x8*)(t + r * RS + 8 * c) = x;
+  }
+  __syncthreads();
+  bf16* dst = vt + ((b * H + h) * ntile + kt) * (int64_t)(D * kTile);
+#pragma unroll
+  for (int s = tid; s < D * (kTile / 8); s += kThreadsT) {
+    const int dr = s / (kTile / 8), c = s % (kTile / 8);
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = t[(8 * c + e) * RS + dr];
+    *(bf16x8*)(dst + dr * kTile + 8 * c) = o;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_v_tiles(const void* v, void* v_tiled, int64_t L, int32_t B, int32_t H, int d, hipStream_t s) {
+  const int64_t nwg = v_tiled_keys(L) / kTile * H * B;
+  if (d == 128) v_tiles_kernel<128><<<dim3((unsigned)nwg), dim3(kThreadsT), 0, s>>>((const bf16*)v, (bf16*)v_tiled, L, H);
+  else v_tiles_kernel<64><<<dim3((unsigned)nwg), dim3(kThreadsT), 0, s>>>((const bf16*)v, (bf16*)v_tiled, L, H);
+  return hipGetLastError();
+}
+
+}  // namespace cpattn
