@@ -298,8 +298,6 @@ cp_status cp_attn_merge_lse(const cp_attn_desc* desc, int32_t n, const float* co
   cp_status st = check_desc(desc);
   if (st != CP_OK) return st;
   if (n < 1 || n > CP_MAX_RING || n > kMaxParts) return fail(CP_ERR_INVALID_ARG, "n=%d outside [1, %d]", n, CP_MAX_RING);
-  if ((int64_t)desc->B * desc->H > 65535)
-    return fail(CP_ERR_UNSUPPORTED, "B*H=%lld above 65535 (one grid row per batch and head)", (long long)desc->B * desc->H);
   if (!o_parts || !lse_parts) return fail(CP_ERR_INVALID_ARG, "o_parts/lse_parts is NULL");
   if ((st = check_tensor(out, "out")) != CP_OK || (st = check_vec(lse_out, "lse_out", true)) != CP_OK) return st;
   MergeArgs a;
@@ -339,8 +337,6 @@ cp_status cp_attn_finalize(const cp_attn_desc* desc, const cp_state* state, void
   cp_status st = check_desc(desc);
   if (st != CP_OK) return st;
   if (!state) return fail(CP_ERR_INVALID_ARG, "state is NULL");
-  if ((int64_t)desc->B * desc->H > 65535)
-    return fail(CP_ERR_UNSUPPORTED, "B*H=%lld above 65535 (one grid row per batch and head)", (long long)desc->B * desc->H);
   if ((st = check_tensor(state->o, "state->o")) != CP_OK || (st = check_vec(state->m, "state->m", false)) != CP_OK ||
       (st = check_vec(state->l, "state->l", false)) != CP_OK || (st = check_tensor(out, "out")) != CP_OK ||
       (st = check_vec(m_out, "m_out", true)) != CP_OK || (st = check_vec(l_out, "l_out", true)) != CP_OK ||

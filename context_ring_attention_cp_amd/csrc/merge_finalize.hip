@@ -8,10 +8,13 @@
 //
 // Both are streaming kernels: each thread owns 8 (merge) or 4 (finalize)
 // consecutive head-dim elements of one (batch, row, head), so a wave
-// reads/writes whole 512-byte rows of float32 with 16-byte accesses.  A workgroup covers consecutive rows
-// of one (batch, head) (grid: row chunks x B*H), so its lse loads are
-// contiguous and a thread finds its row and column with shifts and one
-// 32-bit division per workgroup index rather than 64-bit divisions.
+// reads/writes whole 512-byte rows of float32 with 16-byte accesses.  A
+// workgroup covers consecutive (batch, row, head) triples in memory order
+// (a 1-D grid), so its partial and state reads are one contiguous run; the
+// small lse / m / l loads ([B, H, L]) are the scattered ones, and they stay
+// in the caches (a cache line of them serves 32 rows).  Measured at the
+// merge stress case: 0.112 ms against 0.123 ms with workgroups of rows of
+// one (batch, head).
 #include "kernels.h"
 
 #include <math.h>
@@ -44,20 +47,20 @@ constexpr int kRegParts = 16;
 // Partials loaded back to back before their multiply-adds.
 constexpr int kBatch = 8;
 
-// grid: x = chunk of kThreads / (D / 8) rows, y = b * H + h.  Each thread
-// owns 8 consecutive head-dim elements (two 16-byte loads per part), so a
-// thread keeps 2 kBatch partial loads in flight.
+// grid: one workgroup per kThreads / (D / 8) consecutive (batch, row, head)
+// triples.  Each thread owns 8 consecutive head-dim elements (two 16-byte
+// loads per part), so a thread keeps 2 kBatch partial loads in flight.
 template <int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
-  constexpr int D8 = D / 8;                       // threads per row
-  constexpr int RPW = kThreads / D8;              // rows per workgroup
-  const int bh = blockIdx.y;
-  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
-  const int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / D8;
-  if (row >= a.L) return;
+  constexpr int D8 = D / 8;                       // threads per row-head
+  constexpr int RPW = kThreads / D8;              // row-heads per workgroup
+  const int64_t rowhead = (int64_t)blockIdx.x * RPW + threadIdx.x / D8;   // ((b L) + row) H + h
+  if (rowhead >= (int64_t)a.B * a.L * a.H) return;
+  const int h = (int)(rowhead % a.H);
+  const int64_t bl = rowhead / a.H;
+  const int64_t row = bl % a.L, b = bl / a.L;
   const int x8 = threadIdx.x % D8;
-  const int64_t rowhead = ((int64_t)b * a.L + row) * a.H + h;
-  const int64_t ml = (int64_t)bh * a.L + row;
+  const int64_t ml = (b * a.H + h) * a.L + row;
   const int64_t off = rowhead * D + 8 * x8;
   const int n = a.n;
 
@@ -113,17 +116,19 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   if (x8 == 0 && a.lse_out) a.lse_out[ml] = lse;
 }
 
+// grid: one workgroup per kThreads / (D / 4) consecutive (batch, row, head)
+// triples; each thread owns 4 consecutive head-dim elements.
 template <int D>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalizeArgs a) {
   constexpr int D4 = D / 4;
   constexpr int RPW = kThreads / D4;
-  const int bh = blockIdx.y;
-  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
-  const int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / D4;
-  if (row >= a.L) return;
+  const int64_t rowhead = (int64_t)blockIdx.x * RPW + threadIdx.x / D4;   // ((b L) + row) H + h
+  if (rowhead >= (int64_t)a.B * a.L * a.H) return;
+  const int h = (int)(rowhead % a.H);
+  const int64_t bl = rowhead / a.H;
+  const int64_t row = bl % a.L, b = bl / a.L;
   const int x4 = threadIdx.x % D4;
-  const int64_t rowhead = ((int64_t)b * a.L + row) * a.H + h;
-  const int64_t ml = (int64_t)bh * a.L + row;
+  const int64_t ml = (b * a.H + h) * a.L + row;
   const float l = a.st_l[ml];
   const float m = a.st_m[ml];
   const bool has = l > 0.f;
@@ -139,10 +144,11 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalizeArgs a) {
 
 }  // namespace
 
-// B * H <= 65535 (the grid's y extent) is checked by the caller.
+// The grids (B L H / 16 or / 32 workgroups) stay below 2^31: the caller
+// bounds B L H d / 1024.
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   const int rpw = kThreads / (a.d / 8);
-  const dim3 grid((unsigned)((a.L + rpw - 1) / rpw), (unsigned)(a.B * a.H));
+  const dim3 grid((unsigned)(((int64_t)a.B * a.L * a.H + rpw - 1) / rpw));
   if (a.d == 128) merge_kernel<128><<<grid, dim3(kThreads), 0, s>>>(a);
   else merge_kernel<64><<<grid, dim3(kThreads), 0, s>>>(a);
   return hipGetLastError();
@@ -150,7 +156,7 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
 
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s) {
   const int rpw = kThreads / (a.d / 4);
-  const dim3 grid((unsigned)((a.L + rpw - 1) / rpw), (unsigned)(a.B * a.H));
+  const dim3 grid((unsigned)(((int64_t)a.B * a.L * a.H + rpw - 1) / rpw));
   if (a.d == 128) finalize_kernel<128><<<grid, dim3(kThreads), 0, s>>>(a);
   else finalize_kernel<64><<<grid, dim3(kThreads), 0, s>>>(a);
   return hipGetLastError();

@@ -137,8 +137,7 @@ cp_status cp_attn_block_partial(const cp_attn_desc* desc, int32_t j, int32_t mod
  *   out                : device [B, L, H, d] of desc->dtype;
  *   lse_out            : device [B, H, L] float32, or NULL.
  * Rows where every part is empty get O = 0 and lse = -inf.
- * Errors: CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED (B * H above 65535),
- * CP_ERR_HIP. */
+ * Errors: CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED, CP_ERR_HIP. */
 cp_status cp_attn_merge_lse(const cp_attn_desc* desc, int32_t n, const float* const* o_parts,
                             const float* const* lse_parts, const int32_t* order, void* out,
                             float* lse_out, void* stream);
@@ -146,8 +145,7 @@ cp_status cp_attn_merge_lse(const cp_attn_desc* desc, int32_t n, const float* co
 /* Final step of the recurrence: out = O / l (0 where l = 0) in desc->dtype
  * (bf16 rounded to nearest even), and optionally m_out, l_out and
  * lse_out = m + ln l (device [B, H, L] float32, each may be NULL).
- * Errors: CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED (B * H above 65535),
- * CP_ERR_HIP. */
+ * Errors: CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED, CP_ERR_HIP. */
 cp_status cp_attn_finalize(const cp_attn_desc* desc, const cp_state* state, void* out,
                            float* m_out, float* l_out, float* lse_out, void* stream);
 

@@ -409,15 +409,3 @@ def test_rank_forward_fp8_argument_errors():
     st = call(desc=d1, ks=(P * 4)(FAKE, FAKE, None, None), vs=(P * 4)(FAKE, FAKE, None, None),
               kb=(P * 4)(FAKE, FAKE, None, None), vb=(P * 4)(FAKE, FAKE, None, None), nbytes=need - 1)
     assert st == B.CP_ERR_WORKSPACE
-
-
-def test_merge_and_finalize_refuse_too_many_heads():
-    lib = B.lib()
-    d = _desc(B=2, H=40000)               # B*H = 80000 rows of the merge grid
-    P = ctypes.c_void_p
-    parts = (P * 2)(FAKE, FAKE + 256)
-    st = _status(lib.cp_attn_merge_lse, d.ref, 2, parts, parts, None, FAKE, None, 0x1000)
-    assert st == B.CP_ERR_UNSUPPORTED and "65535" in B.last_error()
-    state = B.cp_state(FAKE, FAKE, FAKE)
-    st = _status(lib.cp_attn_finalize, d.ref, ctypes.byref(state), FAKE, None, None, None, 0x1000)
-    assert st == B.CP_ERR_UNSUPPORTED and "65535" in B.last_error()

@@ -309,6 +309,47 @@ def test_full_size_partial_merge(cp):
 # API corners
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_merge_and_finalize_many_heads(cp, dtype):
+    """merge_lse and finalize with B * H = 80000 (batch, head) pairs and a
+    4-row shard: their 1-D grids walk (batch, row, head) in memory order, so
+    no grid extent bounds B * H.  Checked on sampled heads of both batches."""
+    N, L, H, d, B, r = 2, 4, 40000, 64, 2, 1
+    spec = ShardSpec(S=N * L, N=N, H=H, d=d, dtype=dtype, mask="none", B=B, cfg_id=108)
+    inp = make_inputs(spec, seed=9, ranks=[r])
+    desc = _desc(cp, spec, r)
+    q = dev(inp["q"][r], dtype)
+    kb, vb = _blocks(spec, inp)
+    heads = [0, 1, 20011, H - 1]
+    ref = oracle.rank_attention(inp["q"][r], inp["k"], inp["v"], r, N, "none", heads=heads)
+    big, vec = (B, L, H, d), (B, H, L)
+
+    say(f"[many heads] {dtype} partial_lse + merge")
+    o_parts, lse_parts = [], []
+    for j in range(N):
+        op = torch.full(big, float("nan"), device="cuda")
+        lp = torch.full(vec, float("nan"), device="cuda")
+        cp.cp_attn_block_partial(desc, j, cp.CP_MODE_PARTIAL_LSE, q, kb[j], vb[j], o_part=op, lse_part=lp)
+        o_parts.append(op)
+        lse_parts.append(lp)
+    out, _, _, lse = _outs(spec)
+    cp.cp_attn_merge_lse(desc, o_parts, lse_parts, [1, 0], out, lse)
+    torch.cuda.synchronize()
+    check_o(host(out)[:, :, heads], ref["o"], dtype)
+    check_stat(host(lse)[:, heads], ref["lse"], dtype, "lse")
+    del o_parts, lse_parts
+
+    say(f"[many heads] {dtype} init/accumulate + finalize")
+    st = (torch.zeros(big, device="cuda"), torch.zeros(vec, device="cuda"), torch.zeros(vec, device="cuda"))
+    for t, j in enumerate([1, 0]):
+        cp.cp_attn_block_partial(desc, j, cp.CP_MODE_INIT if t == 0 else cp.CP_MODE_ACCUMULATE, q, kb[j], vb[j],
+                                 state=st)
+    out, m, l, lse = _outs(spec)
+    cp.cp_attn_finalize(desc, st, out, m, l, lse)
+    torch.cuda.synchronize()
+    _check_all((host(out)[:, :, heads], host(m)[:, heads], host(l)[:, heads], host(lse)[:, heads]), ref, dtype)
+
+
 def test_merge_order_null_and_single_part(cp):
     """merge_lse with order = NULL sums in index order (bit-identical to the
     explicit identity order); with one part the output is that part."""
