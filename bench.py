@@ -41,7 +41,7 @@ KERNELS = {
     "bf16": dict(name="attn_block_bf16_kernel<128", srcs=("attn_mfma.hip", "gfx950_util.h", "kernels.h"),
                  json="attn_block_bf16__causal_128k_last_rank.traffic.json", copy_bytes=2 * _BLK,
                  cmd="python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-secondary"),
-    "fp8": dict(name="attn_block_fp8_kernel<128>", srcs=("attn_fp8.hip", "gfx950_util.h", "kernels.h"),
+    "fp8": dict(name="attn_block_fp8_kernel<128", srcs=("attn_fp8.hip", "gfx950_util.h", "kernels.h"),
                 json="attn_block_fp8__causal_128k_last_rank.traffic.json", copy_bytes=_BLK,
                 cmd="python3 bench.py --fp8-only --steps 1 --warmup 0"),
 }

@@ -547,10 +547,10 @@ static cp_status rank_forward_impl(const cp_attn_desc* desc, const void* q, cons
   char* ws = (char*)workspace;
   const size_t blk_bytes = (size_t)desc->B * desc->L * desc->H * desc->d * (fp8 ? 1 : elt_bytes(desc->dtype));
   const int32_t nsteps = (int32_t)sched.size();
-  // bf16 V blocks are received in head-dim-major 64-key tiles (the receive
-  // writes that layout; the attention kernel fetches each tile as one
+  // bf16 and e4m3 V blocks are received in head-dim-major key tiles (the
+  // receive writes that layout; the attention kernel fetches each tile as one
   // contiguous run and reads V^T operands as whole 16-byte rows)
-  const bool v_tiled = !fp8 && desc->dtype == CP_BF16;
+  const bool v_tiled = fp8 || desc->dtype == CP_BF16;
 
   // ready[t]: block of step t is in its slot; done[t]: step t's kernel finished with its slot
   std::vector<hipEvent_t> ready(nsteps, nullptr), done(nsteps, nullptr);
@@ -574,6 +574,7 @@ static cp_status rank_forward_impl(const cp_attn_desc* desc, const void* q, cons
     const int32_t j = sched[t];
     hipError_t r = hipMemcpyAsync(slot_k(t), k_blocks[j], blk_bytes, hipMemcpyDeviceToDevice, s);
     if (r != hipSuccess) return r;
+    if (v_tiled && fp8) return launch_v_tiles_fp8(v_blocks[j], slot_v(t), desc->L, desc->B, desc->H, desc->d, s);
     if (v_tiled) return launch_v_tiles(v_blocks[j], slot_v(t), desc->L, desc->B, desc->H, desc->d, s);
     return hipMemcpyAsync(slot_v(t), v_blocks[j], blk_bytes, hipMemcpyDeviceToDevice, s);
   };

@@ -24,6 +24,12 @@
 //     lane s addresses row base + s/2 at column base + 8(s%2), and lane l
 //     receives column base + l of the 8 rows base .. base+7 (measured on the
 //     device with an index-filled LDS probe).
+// Tiled V (F_V_TILED, the layout the ring's receive writes): V arrives as
+//   [B, H, T, d, 128] (T tiles of 128 keys, each tile head-dim-major, zero
+//   past L), with the keys of each 64-key half stored in the order the A
+//   operand consumes them (key 16 q + 8 g + e at position 32 g + 8 q + e), so
+//   the 32 bytes of lane half g are contiguous: two 16-byte LDS reads per
+//   operand instead of four transpose loads.
 // Scales: S = s_q s_k (codes product), folded into the exp2 coefficient; the
 //   accumulator holds sum P V_codes, so the running state is divided by s_v
 //   on load and O multiplied by s_v before it is stored.
@@ -75,7 +81,7 @@ __device__ __forceinline__ floatx16 mfma8(const int8v& a, const int8v& b, const 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-template <int D>
+template <int D, bool VT>
 __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
   constexpr int CH = D / 16;         // 16-byte chunks per row
   constexpr int NS = D / 64;         // k-steps of S^T = K Q^T
@@ -108,7 +114,9 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
   const int64_t base = (int64_t)b * L * rs + (int64_t)h * D;
   const uint8_t* __restrict__ qg = (const uint8_t*)a.q + base;
   const uint8_t* __restrict__ kg = (const uint8_t*)a.k + base;
-  const uint8_t* __restrict__ vg = (const uint8_t*)a.v + base;
+  // tiled V: this head's tiles of D x BN bytes, one after another
+  const int64_t nkt_all = (L + BN - 1) / BN;
+  const uint8_t* __restrict__ vg = (const uint8_t*)a.v + (VT ? ((int64_t)b * H + h) * D * nkt_all * BN : base);
   const int bh = b * H + h;
   const float s_qk = a.q_scale[bh] * a.k_scale[bh];
   const float s_v = a.v_scale[bh];
@@ -203,6 +211,16 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
   const uint32_t f_off = (uint32_t)((int64_t)f_row * rs + 16 * (f_ph ^ swz8<D>(f_row)));
   const uint32_t smem_base = lds_addr(&smem[0][0][0]);
   auto lds_of = [&](int st, int tensor, int byte) { return smem_base + (uint32_t)((st * 2 + tensor) * TILE + byte); };
+  // Tiled V: a tile is D rows of BN bytes (CHT chunks), stored contiguously;
+  // fetch i of a lane fills row i * RPST + f_tid / CHT, physical chunk
+  // f_tid % CHT, with the swizzle of 128-byte rows.  Keys past L are zero
+  // codes in the block itself, so every tile is read whole.
+  constexpr int CHT = BN / 16;
+  constexpr int RPST = kFetchThreads / CHT;
+  static_assert(D * CHT == BN * CH && RPST % 16 == 0, "tiled V fetch split");
+  const int ft_row = f_tid / CHT;
+  const uint32_t fvt_off = (uint32_t)(ft_row * BN + 16 * ((f_tid % CHT) ^ swz8<BN>(ft_row)));
+  auto fetch_vt = [&](int kt, int i, uint32_t lds) { fetch16(vg + ((int64_t)kt * D + i * RPST) * BN, fvt_off, lds); };
   auto fetch = [&](int kt, int st) {
     const int64_t key0 = (int64_t)kt * BN;
     if (key0 + BN <= L) {
@@ -211,7 +229,8 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
         const int64_t rowoff = (key0 + i * RPS) * rs;
         const int wbase = (i * kFetchThreads + 64 * f_w) * 16;
         fetch16(kg + rowoff, f_off, lds_of(st, 0, wbase));
-        fetch16(vg + rowoff, f_off, lds_of(st, 1, wbase));
+        if constexpr (VT) fetch_vt(kt, i, lds_of(st, 1, wbase));
+        else fetch16(vg + rowoff, f_off, lds_of(st, 1, wbase));
       }
     } else {
       // the ragged last tile: offsets relative to its first row; rows past the
@@ -223,7 +242,8 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
         const uint32_t off = (uint32_t)(rrow * rs + 16 * (f_ph ^ swz8<D>(f_row)));
         const int wbase = (i * kFetchThreads + 64 * f_w) * 16;
         fetch16(kg + key0 * rs, off, lds_of(st, 0, wbase));
-        fetch16(vg + key0 * rs, off, lds_of(st, 1, wbase));
+        if constexpr (VT) fetch_vt(kt, i, lds_of(st, 1, wbase));
+        else fetch16(vg + key0 * rs, off, lds_of(st, 1, wbase));
       }
     }
   };
@@ -244,6 +264,14 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
     return int8v{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
   auto rd_v = [&](const uint8_t* __restrict__ Vs, int kh, int dt) {
+    if constexpr (VT) {
+      // row 32 dt + r32 of V^T, the 32 bytes of half g of key half kh: logical chunks 4 kh + 2 g and + 1
+      const int row = 32 * dt + r32;
+      const uint8_t* rp = Vs + row * BN;
+      const uint4 lo = *(const uint4*)(rp + 16 * ((4 * kh + 2 * g) ^ swz8<BN>(row)));
+      const uint4 hi = *(const uint4*)(rp + 16 * ((4 * kh + 2 * g + 1) ^ swz8<BN>(row)));
+      return int8v{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
     const int col = 32 * dt + tr_col;
     int2v x[4];
 #pragma unroll
@@ -472,8 +500,14 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
 hipError_t launch_block_fp8(const BlockArgs& a, int d, hipStream_t s) {
   const int64_t nqt = (a.L + BM - 1) / BM;
   const int64_t nwg = nqt * a.H * a.B;
-  if (d == 128) attn_block_fp8_kernel<128><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
-  else attn_block_fp8_kernel<64><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
+  const bool vt = (a.flags & F_V_TILED) != 0;
+  if (d == 128) {
+    if (vt) attn_block_fp8_kernel<128, true><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
+    else attn_block_fp8_kernel<128, false><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
+  } else {
+    if (vt) attn_block_fp8_kernel<64, true><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
+    else attn_block_fp8_kernel<64, false><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

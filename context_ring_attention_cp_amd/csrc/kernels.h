@@ -12,7 +12,8 @@ enum : int32_t {
   F_WRITE_STATE = 2,    // store the running state
   F_WRITE_FINAL = 4,    // store out = O / l (input dtype) and m, l, lse
   F_WRITE_PARTIAL = 8,  // store normalised O (float32) and lse of this block alone
-  F_V_TILED = 16,       // bf16 only: v in head-dim-major 64-key tiles [B, H, T, d, 64], zero past L
+  F_V_TILED = 16,       // v in head-dim-major key tiles, zero past L: bf16 [B, H, T, d, 64],
+                        // e4m3 [B, H, T8, d, 128] with the operand key order (launch_v_tiles_fp8)
 };
 
 // Keys of a tiled V block: L rounded up to whole 64-key tiles (T = that / 64).
@@ -115,6 +116,10 @@ hipError_t launch_block_f32(const BlockArgs& a, int d, hipStream_t s);
 // bf16 V block [B, L, H, d] -> the tiled layout F_V_TILED reads, keys L..
 // filled with zeros.
 hipError_t launch_v_tiles(const void* v, void* v_tiled, int64_t L, int32_t B, int32_t H, int d, hipStream_t s);
+// e4m3 V codes [B, L, H, d] -> [B, H, T8, d, 128] (T8 = ceil(L / 128)), each
+// 64-key half in the order the FP8 MFMA's A operand consumes keys, zero codes
+// from L on.
+hipError_t launch_v_tiles_fp8(const void* v, void* v_tiled, int64_t L, int32_t B, int32_t H, int d, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
 hipError_t launch_bwd_delta(const DeltaArgs& a, int d, hipStream_t s);

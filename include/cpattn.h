@@ -163,9 +163,9 @@ size_t cp_attn_workspace_bytes(const cp_attn_desc* desc);
  * row can see are skipped (causal: j > rank; documents: blocks that end before
  * the document of the shard's first token begins).  Every step after the
  * first receives its block into one of two workspace slots with a
- * device-to-device copy (for bf16, V is written in head-dim-major tiles of
- * 64 keys, the layout the attention kernel reads best; the caller's blocks
- * are only read); with CP_RING_PREFETCH the copy runs on copy_stream
+ * device-to-device copy (V is written in head-dim-major key tiles, the
+ * layout the attention kernels read best; the caller's blocks are only
+ * read); with CP_RING_PREFETCH the copy runs on copy_stream
  * while the previous block is computed (events order slot reuse), otherwise
  * it runs on compute_stream.  The last step writes the final output.
  *   out          : device [B, L, H, d] of desc->dtype;
