@@ -4,7 +4,7 @@
 // validates all of its arguments before it makes any HIP call, so invalid
 // calls fail without touching a device.
 #include "cpattn.h"
-#include "kernels.h"
+#include "launch.h"
 
 #include <hip/hip_runtime.h>
 
@@ -786,17 +786,21 @@ cp_status cp_attn_ulysses_forward(const cp_attn_desc* desc, const void* const* q
   ra.d = desc->d;
   ra.elt = (int32_t)elt_bytes(desc->dtype);
   hipError_t e = hipSuccess;
+  // bf16 V over whole 64-key tiles is gathered straight into the tiled layout
+  // (the same bytes; the attention kernel reads V^T operands as 16-byte rows)
+  const bool v_tiled = desc->dtype == CP_BF16 && full.L % 64 == 0;
   // step 1: the first all-to-all, as seen by this rank (its heads of every shard)
   const void* const* srcs[3] = {q_shards, k_shards, v_shards};
   void* dsts[3] = {qf, kf, vf};
   for (int x = 0; x < 3; ++x) {
     for (int32_t i = 0; i < desc->N; ++i) ra.shards[i] = const_cast<void*>(srcs[x][i]);
     ra.full = dsts[x];
-    if ((e = launch_a2a_gather(ra, s)) != hipSuccess) return hip_fail(e, "all-to-all gather launch");
+    e = (x == 2 && v_tiled) ? launch_a2a_gather_v_tiles(ra, s) : launch_a2a_gather(ra, s);
+    if (e != hipSuccess) return hip_fail(e, "all-to-all gather launch");
   }
   // step 2: attention over the whole sequence for this rank's heads
   BlockArgs a = block_args(&full, 0, qf, kf, vf);
-  a.flags = F_WRITE_FINAL;
+  a.flags = F_WRITE_FINAL | (v_tiled ? F_V_TILED : 0);
   a.out = of;
   a.m_out = m_out;
   a.l_out = l_out;

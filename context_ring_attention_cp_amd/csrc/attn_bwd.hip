@@ -30,7 +30,7 @@
 // consecutive rows, exactly the B operand of the next product's k-step h.
 // The LDS tiles of both kernels are read both as MFMA operand rows and by the
 // transpose loads; swz_kv below keeps both patterns free of bank conflicts.
-#include "kernels.h"
+#include "launch.h"
 #include "gfx950_util.h"
 
 #include <math.h>

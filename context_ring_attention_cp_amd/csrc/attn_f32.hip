@@ -8,7 +8,7 @@
 // fits in registers for d = 128), and a score is the sum of the four lanes'
 // partial dot products.  A workgroup of 256 lanes covers 64 rows and stages
 // key tiles of 16 keys of K and V in LDS.
-#include "kernels.h"
+#include "launch.h"
 
 #include <math.h>
 

@@ -46,7 +46,7 @@
 //   phase's fixed costs (barriers, waits, the row max exchange); 128-key tiles
 //   were 5 % faster on the same device.  The operands are read 2 MFMAs ahead,
 //   which keeps the kernel within 256 VGPRs.
-#include "kernels.h"
+#include "launch.h"
 #include "gfx950_util.h"
 
 #include <math.h>

@@ -50,7 +50,7 @@
 // P <= 256 in between.  O / l is unchanged by the choice of reference; at the
 // end O and l are rescaled once to the true running max, which is what the
 // state and the outputs hold.
-#include "kernels.h"
+#include "launch.h"
 #include "gfx950_util.h"
 
 #include <math.h>

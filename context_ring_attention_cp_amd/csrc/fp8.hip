@@ -14,7 +14,7 @@
 // float bits (order-preserving for non-negative floats), the codes, then the
 // scales.  Each thread handles 8 consecutive elements of one token row of one
 // head; a workgroup covers kRowsPerWg rows of one (b, h).
-#include "kernels.h"
+#include "launch.h"
 
 #include <stdint.h>
 

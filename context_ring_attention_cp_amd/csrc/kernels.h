@@ -1,5 +1,6 @@
-// Internal interface between the host API (api.cpp) and the HIP kernels.
-// Not part of the public ABI.
+// Internal interface between the host API (api.cpp) and the HIP kernels:
+// the flags, layouts and argument structs the kernels are compiled against.
+// The launcher declarations are in launch.h.  Not part of the public ABI.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -110,22 +111,6 @@ struct DeltaArgs {
   float* delta;          // [B, H, L]
 };
 
-// Launchers return the hipError_t of the launch.
-hipError_t launch_block_bf16(const BlockArgs& a, int d, hipStream_t s);
-hipError_t launch_block_f32(const BlockArgs& a, int d, hipStream_t s);
-// bf16 V block [B, L, H, d] -> the tiled layout F_V_TILED reads, keys L..
-// filled with zeros.
-hipError_t launch_v_tiles(const void* v, void* v_tiled, int64_t L, int32_t B, int32_t H, int d, hipStream_t s);
-// e4m3 V codes [B, L, H, d] -> [B, H, T8, d, 128] (T8 = ceil(L / 128)), each
-// 64-key half in the order the FP8 MFMA's A operand consumes keys, zero codes
-// from L on.
-hipError_t launch_v_tiles_fp8(const void* v, void* v_tiled, int64_t L, int32_t B, int32_t H, int d, hipStream_t s);
-hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
-hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
-hipError_t launch_bwd_delta(const DeltaArgs& a, int d, hipStream_t s);
-hipError_t launch_bwd_blocks(const BwdArgs& a, int d, hipStream_t s);   // dq kernel, then dk/dv kernel
-hipError_t launch_zero(float* p, int64_t n, hipStream_t s);            // n a multiple of 4
-
 // Regrouping of all-to-all (Ulysses) context parallelism between the N
 // sequence shards [B, L, H, d] and the whole sequence of one rank's head
 // group [h0, h0 + Hn), stored [B, S, Hn, d] (S = N L).  Element bytes elt; Hn d
@@ -137,8 +122,6 @@ struct RegroupArgs {
   int64_t B, L, S;
   int32_t N, H, Hn, h0, d, elt;
 };
-hipError_t launch_a2a_gather(const RegroupArgs& a, hipStream_t s);
-hipError_t launch_a2a_scatter(const RegroupArgs& a, hipStream_t s);
 
 // FP8 (e4m3) quantisation of a bf16 block [B, L, H, d] with one scale per
 // (b, h): codes [B, L, H, d] bytes, scales [B, H] float32 (amax / 448).
@@ -149,8 +132,5 @@ struct QuantArgs {
   int64_t L;
   int32_t B, H;
 };
-hipError_t launch_quantize_fp8(const QuantArgs& a, int d, hipStream_t s);
-// FP8 (e4m3) inputs, bf16 output; the same flags and state as the bf16 kernel.
-hipError_t launch_block_fp8(const BlockArgs& a, int d, hipStream_t s);
 
 }  // namespace cpattn

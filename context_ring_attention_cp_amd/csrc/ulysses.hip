@@ -11,7 +11,13 @@
 // group is one contiguous run of Hn d elements in both layouts; each thread
 // moves 16 bytes, consecutive threads consecutive bytes of a run.  The
 // second grid dimension is the shard, so the shard pointer is a uniform load.
-#include "kernels.h"
+//
+// For bf16 V over a sequence of whole 64-key tiles the gather writes the
+// tiled layout the attention kernel reads best instead ([B, Hn, S / 64, d,
+// 64]: each 64-key tile head-dim-major and contiguous), taking each key row
+// from whichever shard holds it.
+#include "launch.h"
+#include "gfx950_util.h"
 
 #include <stdint.h>
 
@@ -52,7 +58,52 @@ hipError_t launch_a2a(const RegroupArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// One workgroup per (batch, head of the group, 64-key tile of the whole
+// sequence): the tile's rows go through LDS (rows padded by 16 bytes), then
+// every lane writes 16-byte runs of 8 consecutive keys of one head-dim row.
+template <int D>
+__global__ __launch_bounds__(kThreads) void a2a_gather_v_tiles_kernel(RegroupArgs a) {
+  using dev::bf16;
+  using dev::bf16x8;
+  constexpr int kT = 64;
+  constexpr int CH = D / 8;
+  constexpr int RS = D + 8;
+  __shared__ __attribute__((aligned(16))) bf16 t[kT * RS];
+  const int64_t ntile = a.S / kT;
+  const int64_t bid = blockIdx.x;
+  const int64_t kt = bid % ntile;
+  const int64_t hb = bid / ntile;
+  const int h = (int)(hb % a.Hn);
+  const int64_t b = hb / a.Hn;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int s = tid; s < kT * CH; s += kThreads) {
+    const int r = s / CH, c = s % CH;
+    const int64_t key = kt * kT + r;                          // position in the whole sequence
+    const int64_t i = key / a.L, tt = key - i * a.L;          // its shard and row there
+    const bf16* src = (const bf16*)a.shards[i] + ((b * a.L + tt) * a.H + a.h0 + h) * D + 8 * c;
+    *(bf16x8*)(t + r * RS + 8 * c) = *(const bf16x8*)src;
+  }
+  __syncthreads();
+  bf16* dst = (bf16*)a.full + ((b * a.Hn + h) * ntile + kt) * (int64_t)(D * kT);
+#pragma unroll
+  for (int s = tid; s < D * (kT / 8); s += kThreads) {
+    const int dr = s / (kT / 8), c = s % (kT / 8);
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = t[(8 * c + e) * RS + dr];
+    *(bf16x8*)(dst + dr * kT + 8 * c) = o;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_a2a_gather_v_tiles(const RegroupArgs& a, hipStream_t s) {
+  const int64_t nwg = a.B * a.Hn * (a.S / 64);
+  if (a.d == 128) a2a_gather_v_tiles_kernel<128><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
+  else a2a_gather_v_tiles_kernel<64><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_a2a_gather(const RegroupArgs& a, hipStream_t s) { return launch_a2a<true>(a, s); }
 hipError_t launch_a2a_scatter(const RegroupArgs& a, hipStream_t s) { return launch_a2a<false>(a, s); }

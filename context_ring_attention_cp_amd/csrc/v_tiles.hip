@@ -15,7 +15,7 @@
 // 32 g + 8 q + e: the order in which the FP8 MFMA's A operand consumes keys
 // (byte e of lane half g stands for key 16 (e / 8) + 8 g + e % 8), so the 32
 // bytes of a lane half are contiguous.
-#include "kernels.h"
+#include "launch.h"
 #include "gfx950_util.h"
 
 namespace cpattn {

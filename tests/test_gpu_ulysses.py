@@ -98,6 +98,18 @@ def test_small_every_rank(cp, dtype, d, mask):
     _every_rank(cp, spec, seed=2)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", ["none", "doc_causal"])
+@pytest.mark.parametrize("N,L", [(4, 48), (2, 96)])
+def test_whole_tile_sequences(cp, d, mask, N, L):
+    """bf16 over a whole number of 64-key tiles (S = 192): V is gathered
+    straight into the tiled layout, and shard boundaries fall inside tiles."""
+    H, B = 2 * N, 2
+    spec = ShardSpec(S=N * L, N=N, H=H, d=d, dtype="bf16", mask=mask, B=B, cfg_id=203,
+                     cu_seqlens=_small_cu(N * L) if mask == "doc_causal" else None)
+    _every_rank(cp, spec, seed=4)
+
+
 @pytest.mark.parametrize("N,L,H", [(1, 333, 2), (4, 70, 4), (8, 40, 8)])
 def test_degenerate_groups(cp, N, L, H):
     """One rank (plain attention of one shard), and one head per rank."""
