@@ -137,6 +137,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def attn_flops(spec, pairs: int) -> float:
+    """Causal-adjusted forward flops: 4 d per visible (query, key) pair (2 d
+    for QK^T, 2 d for PV) of each batch element and head; `pairs` is the
+    per-(batch, head) count of cp_attn_visible_pairs."""
+    return 4.0 * spec.d * spec.B * spec.H * pairs
+
+
 def cpu_baseline(spec, q, k, v, rows_n: int):
     """The fp64 oracle, as it is, on a bounded sample of the same workload:
     `rows_n` evenly spaced query rows of head 0, against all keys."""
@@ -153,7 +160,7 @@ def cpu_baseline(spec, q, k, v, rows_n: int):
     dt = time.perf_counter() - t0
     p = spec.rank * L + rows
     pairs = int(np.sum(p + 1)) if spec.mask == "causal" else int(rows_n * spec.S)
-    flops = 4.0 * spec.d * pairs
+    flops = 4.0 * spec.d * pairs          # one head, one batch element: the sample
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": f"{rows_n} evenly spaced query rows of head 0 of {spec.H} ({pairs} visible pairs, "
                       f"{dt:.1f} s wall, fp64 numpy, materialised score rows)",
@@ -240,7 +247,7 @@ def secondary(seed: int, reps: int = 5):
         ws = cp.alloc_workspace(desc)
         run = lambda: cp.cp_attn_rank_forward(desc, q, kb, vb, o, None, None, lse, workspace=ws,  # noqa: E731
                                               compute_stream=cs, copy_stream=xs, flags=cp.CP_RING_PREFETCH)
-        fl = 4.0 * spec.d * spec.H * cp.cp_attn_visible_pairs(desc)
+        fl = attn_flops(spec, cp.cp_attn_visible_pairs(desc))
         if cfg == 2:
             # K/V of this shard (4 x 32 MiB) would stay in the caches between iterations
             t = _timed_flushed(run, cs, 3, 10, flush)
@@ -277,7 +284,7 @@ def secondary(seed: int, reps: int = 5):
     tp = _timed_flushed(partials, cs, 2, 10, flush)
     tm = _timed_flushed(merge, cs, 3, 10, flush)
     ms_p, ms_m = tp["median"], tm["median"]
-    fl = 4.0 * spec.d * spec.H * cp.cp_attn_visible_pairs(desc)
+    fl = attn_flops(spec, cp.cp_attn_visible_pairs(desc))
     rows = spec.L * spec.H
     merge_bytes = spec.N * rows * (spec.d * 4 + 4) + rows * (spec.d * 2 + 4)
     out["cfg4"] = {"workload": spec.name, "order": order, "timing": "median of 10, caches flushed between iterations",
@@ -364,7 +371,7 @@ def fp8_forward(cp, spec, seed: int, cs, xs, reps: int) -> dict:
     kms = prof.read()
     prof.close()
     assert torch.isfinite(o.float()).all(), "non-finite FP8 output"
-    fl = 4.0 * spec.d * spec.B * spec.H * cp.cp_attn_visible_pairs(desc)
+    fl = attn_flops(spec, cp.cp_attn_visible_pairs(desc))
     k_tf = fl * reps / (sum(kms) * 1e-3) / 1e12
     res = {"workload": "causal last-rank shard of the 128K example with e4m3 Q/K/V (per-(batch, head) scales), "
                        "bf16 output: S=131072 N=4 L=32768 rank=3 B=1 H=32 d=128, ring prefetch",
@@ -452,7 +459,7 @@ def main():
     sched = cp.cp_attn_ring_schedule(desc, cp.CP_RING_PREFETCH)
     prof = cp.Profiler(len(sched) * max(args.steps, 1))
     pairs = cp.cp_attn_visible_pairs(desc)
-    flops = 4.0 * d * spec.B * H * pairs
+    flops = attn_flops(spec, pairs)
     torch.cuda.synchronize()
 
     def step(p=None):

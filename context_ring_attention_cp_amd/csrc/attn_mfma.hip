@@ -11,7 +11,7 @@
 // Work split: a workgroup of 8 waves (two per SIMD) owns BM = 256 query rows
 // of one (batch, head); each wave owns 32 rows.  Key tiles of BN = 64 keys of
 // K and V are fetched straight into LDS (global_load_lds, 16 B per lane) in a
-// ring of 3 stages and shared by the 8 waves.
+// ring of 4 stages and shared by the 8 waves.
 //
 // MFMA orientation (v_mfma_f32_32x32x16_bf16, D = A x B + C, A 32x16, B 16x32):
 //   S^T = K Q^T : A = K tile (rows = keys, k = head dim), B = Q^T (k = head

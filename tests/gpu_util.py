@@ -90,3 +90,52 @@ def sample_rows(L: int, seed: int, n_random: int = 192, extra=()) -> np.ndarray:
     rows.update(int(x) for x in extra)
     rows.update(int(x) for x in rng.choice(L, size=min(n_random, L), replace=False))
     return np.asarray(sorted(r for r in rows if 0 <= r < L), dtype=np.int64)
+
+
+def oracle_workers() -> int:
+    """Threads for running oracle calls side by side: the host's cores, at
+    most 16 (each call then uses one BLAS thread)."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def pooled_map(fn, items, workers: int = 0):
+    """``[fn(x) for x in items]`` on a thread pool, one BLAS thread per call.
+    numpy's matrix products and ufuncs release the GIL, so the calls run in
+    parallel; each call is the unchanged oracle function on its own part."""
+    import concurrent.futures as cf
+
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        with cf.ThreadPoolExecutor(workers or oracle_workers()) as ex:
+            return list(ex.map(fn, items))
+
+
+def pooled_rows(fn, n_rows: int, chunk: int = 256, workers: int = 0):
+    """``fn(rows)`` over consecutive row chunks [r0, r0 + chunk) of
+    range(n_rows) (see pooled_map), results in row order."""
+    chunks = [np.arange(r0, min(r0 + chunk, n_rows), dtype=np.int64) for r0 in range(0, n_rows, chunk)]
+    return pooled_map(fn, chunks, workers)
+
+
+def pooled_reduce(fn, n_rows: int, chunk: int = 256, workers: int = 0):
+    """Like pooled_rows, but each worker thread takes a contiguous share of
+    the chunks and folds the results of its chunks with ``fn(rows, acc) ->
+    acc`` (acc is None for a worker's first chunk); returns the list of the
+    workers' accumulators, in row order of their shares."""
+    import concurrent.futures as cf
+
+    from threadpoolctl import threadpool_limits
+    nw = workers or oracle_workers()
+    starts = list(range(0, n_rows, chunk))
+    shares = [starts[len(starts) * w // nw: len(starts) * (w + 1) // nw] for w in range(nw)]
+
+    def run(share):
+        acc = None
+        for r0 in share:
+            acc = fn(np.arange(r0, min(r0 + chunk, n_rows), dtype=np.int64), acc)
+        return acc
+
+    with threadpool_limits(1):
+        with cf.ThreadPoolExecutor(nw) as ex:
+            return [a for a in ex.map(run, shares) if a is not None]

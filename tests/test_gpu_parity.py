@@ -14,7 +14,7 @@ import pytest
 import oracle
 from harness.inputs import (TENSOR_K, TENSOR_Q, TENSOR_V, ShardSpec, draw_shard, make_inputs,
                             normal_block, shuffled_order, standard_configs)
-from tests.gpu_util import check_o, check_stat, dev, host, sample_rows, say
+from tests.gpu_util import check_o, check_stat, dev, host, pooled_map, pooled_rows, sample_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -249,10 +249,31 @@ def _heads(spec, seed):
     return sorted({0, spec.H - 1, int(rng.integers(spec.H))})
 
 
+def _oracle_whole_head(spec, q, k, v, h):
+    """The definition for every row of head h of a B = 1 shard, in row chunks
+    on a thread pool: O [1, L, 1, d] and m, l, lse [1, 1, L]."""
+    blocks = sorted(k)
+    K = np.concatenate([k[j][0, :, h, :] for j in blocks]).astype(np.float64)
+    V = np.concatenate([v[j][0, :, h, :] for j in blocks]).astype(np.float64)
+    c = np.concatenate([np.arange(j * spec.L, (j + 1) * spec.L, dtype=np.int64) for j in blocks])
+
+    def part(rows):
+        return oracle.attention_rows(q[0, rows, h, :], K, V, spec.rank * spec.L + rows, c, spec.mask,
+                                     spec.cu_seqlens)
+
+    parts = pooled_rows(part, spec.L)
+    o = np.concatenate([x[0] for x in parts])[None, :, None, :]
+    m, l, lse = (np.concatenate([x[i] for x in parts])[None, None, :] for i in (1, 2, 3))
+    return {"o": o, "m": m, "l": l, "lse": lse}
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfg", [2, 3, 5])
 def test_full_size_rank_forward(cp, cfg):
     """The causal 32K and 128K last-rank shards and the packed-document shard
-    at full size, ring prefetch on, sampled rows against the oracle."""
+    at full size, ring prefetch on: one whole head element by element, and in
+    every head the first and last row of every 256-row query tile plus rows
+    at document boundaries and a seeded random set, against the oracle."""
     spec = standard_configs(seed=0)[cfg]
     blocks = oracle.ring_schedule(spec.N, spec.rank, spec.L, spec.mask, spec.cu_seqlens)
     say(f"[full cfg {cfg}] {spec.name}: blocks {blocks}")
@@ -260,19 +281,29 @@ def test_full_size_rank_forward(cp, cfg):
     kb = [dev(k[j], "bf16") if j in k else None for j in range(spec.N)]
     vb = [dev(v[j], "bf16") if j in v else None for j in range(spec.N)]
     got = run_rank(cp, spec, spec.rank, dev(q, "bf16"), kb, vb, cp.CP_RING_PREFETCH)
-    extra = []
+    for arr in got:
+        assert np.all(np.isfinite(arr))
+
+    h = int(np.random.default_rng(100 + cfg).integers(spec.H))
+    say(f"[full cfg {cfg}] oracle: all {spec.L} rows of head {h}")
+    ref = _oracle_whole_head(spec, q, k, v, h)
+    stats = _check_all(got, ref, "bf16", rows=np.arange(spec.L), heads=[h])
+    say(f"[full cfg {cfg}] whole head {h}: {stats}")
+
+    extra = [t * 256 for t in range((spec.L + 255) // 256)] + [min(t * 256 + 255, spec.L - 1)
+                                                                for t in range((spec.L + 255) // 256)]
     if spec.cu_seqlens is not None:
         s0 = spec.rank * spec.L
         for x in spec.cu_seqlens:
             if s0 <= x < s0 + spec.L:
                 extra += [x - s0 - 1, x - s0, x - s0 + 1]
-    rows = sample_rows(spec.L, cfg, extra=extra)
-    heads = _heads(spec, cfg)
-    ref = oracle.rank_attention(q, k, v, spec.rank, spec.N, spec.mask, spec.cu_seqlens, rows=rows, heads=heads)
-    stats = _check_all(got, ref, "bf16", rows=rows, heads=heads)
-    say(f"[full cfg {cfg}] {len(rows)} rows x {len(heads)} heads: {stats}")
-    for arr in got:
-        assert np.all(np.isfinite(arr))
+    rows = sample_rows(spec.L, cfg, n_random=64, extra=extra)
+    say(f"[full cfg {cfg}] oracle: {len(rows)} rows x {spec.H} heads")
+    per_head = pooled_map(lambda hh: oracle.rank_attention(q, k, v, spec.rank, spec.N, spec.mask, spec.cu_seqlens,
+                                                           rows=rows, heads=[hh]), range(spec.H))
+    ref = {key: np.concatenate([x[key] for x in per_head], axis=2 if key == "o" else 1) for key in per_head[0]}
+    stats = _check_all(got, ref, "bf16", rows=rows, heads=list(range(spec.H)))
+    say(f"[full cfg {cfg}] {len(rows)} rows x {spec.H} heads: {stats}")
 
 
 def test_full_size_partial_merge(cp):
