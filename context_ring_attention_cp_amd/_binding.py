@@ -126,7 +126,9 @@ def _check(status: int) -> None:
 class Desc:
     """Python owner of a cp_attn_desc and of the host cu_seqlens it points to.
 
-    ``cu_seqlens_dev`` is a device int32 tensor (the caller keeps it alive).
+    ``cu_seqlens_dev`` is a device int32 tensor; the Desc holds a reference
+    to it, so it lives as long as the Desc (kernels enqueued with the Desc read
+    it asynchronously).
     """
 
     def __init__(self, B: int, H: int, d: int, N: int, L: int, rank: int, dtype: str = "bf16",
@@ -142,6 +144,7 @@ class Desc:
             self._cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
             self.c.cu_seqlens = self._cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
             self.c.ndocs = int(self._cu.shape[0] - 1)
+        self._cu_dev = cu_seqlens_dev
         if cu_seqlens_dev is not None:
             self.c.cu_seqlens_dev = _ptr(cu_seqlens_dev)
         self.dtype = dtype
