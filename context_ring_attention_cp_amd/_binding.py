@@ -23,6 +23,7 @@ CP_F32, CP_BF16 = 0, 1
 CP_MODE_INIT, CP_MODE_ACCUMULATE, CP_MODE_PARTIAL_LSE = 0, 1, 2
 CP_RING_PREFETCH, CP_RING_REVERSE = 1, 2
 CP_MAX_RING = 64
+CP_STATIC_SCRATCH_BYTES = 64 << 20
 
 MASKS = {"none": CP_MASK_NONE, "causal": CP_MASK_CAUSAL, "doc_causal": CP_MASK_DOC_CAUSAL}
 DTYPES = {"f32": CP_F32, "bf16": CP_BF16}
@@ -34,7 +35,7 @@ EXPORTED = [
     "cp_attn_profiler_destroy", "cp_attn_status_string", "cp_attn_last_error",
     "cp_attn_bwd_delta", "cp_attn_block_backward", "cp_attn_rank_backward",
     "cp_attn_ulysses_workspace_bytes", "cp_attn_ulysses_forward", "cp_attn_quantize_fp8",
-    "cp_attn_rank_forward_fp8",
+    "cp_attn_rank_forward_fp8", "cp_attn_rank_forward_static",
 ]
 
 
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.cp_attn_workspace_bytes.restype = ctypes.c_size_t
         L.cp_attn_rank_forward.argtypes = [dp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, f32p, f32p,
                                            f32p, vp, ctypes.c_size_t, vp, vp, i32, vp]
+        L.cp_attn_rank_forward_static.argtypes = [dp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, f32p, f32p,
+                                                  f32p, vp, vp, i32, vp]
         L.cp_attn_ring_schedule.argtypes = [dp, i32, ctypes.POINTER(i32), i32, ctypes.POINTER(i32)]
         L.cp_attn_visible_pairs.argtypes = [dp, ctypes.POINTER(i64)]
         L.cp_attn_profiler_create.argtypes = [i32, ctypes.POINTER(vp)]
@@ -283,6 +286,31 @@ def cp_attn_rank_forward(desc: Desc, q, k_blocks: Sequence, v_blocks: Sequence, 
                                       _ptr(lse_out), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), cs, xs, int(flags),
                                       profiler.handle if profiler is not None else None))
+
+
+def cp_attn_rank_forward_static(desc: Desc, q, k_blocks: Sequence, v_blocks: Sequence, out, m_out=None,
+                                l_out=None, lse_out=None, compute_stream=None, copy_stream=None,
+                                flags: int = CP_RING_PREFETCH, profiler: Optional["Profiler"] = None) -> None:
+    """cp_attn_rank_forward with the library's static scratch as workspace."""
+    import torch
+    big, vec = _shapes(desc)
+    dt = _io_dtype(desc)
+    N = desc.c.N
+    if len(k_blocks) != N or len(v_blocks) != N:
+        raise ValueError(f"need N={N} K and V block entries (None for blocks that are never visited)")
+    _check_tensor(q, "q", big, dt)
+    for t in list(k_blocks) + list(v_blocks):
+        _check_tensor(t, "k/v block", big, dt)
+    _check_tensor(out, "out", big, dt)
+    for n, t in (("m_out", m_out), ("l_out", l_out), ("lse_out", lse_out)):
+        _check_tensor(t, n, vec, torch.float32)
+    kp = (ctypes.c_void_p * N)(*[_ptr(t) for t in k_blocks])
+    vp = (ctypes.c_void_p * N)(*[_ptr(t) for t in v_blocks])
+    cs = _stream(compute_stream)
+    xs = _stream(copy_stream) if copy_stream is not None else cs
+    _check(lib().cp_attn_rank_forward_static(desc.ref, _ptr(q), kp, vp, _ptr(out), _ptr(m_out), _ptr(l_out),
+                                             _ptr(lse_out), cs, xs, int(flags),
+                                             profiler.handle if profiler is not None else None))
 
 
 def cp_attn_ulysses_workspace_bytes(desc: Desc) -> int:

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcpattn.so")
 
-SOURCES = ["api.cpp", "attn_mfma.hip", "attn_f32.hip", "merge_finalize.hip", "attn_bwd.hip", "ulysses.hip", "fp8.hip", "attn_fp8.hip", "v_tiles.hip"]
+SOURCES = ["api.cpp", "attn_mfma.hip", "attn_f32.hip", "merge_finalize.hip", "attn_bwd.hip", "ulysses.hip", "fp8.hip", "attn_fp8.hip", "v_tiles.hip", "scratch.hip"]
 
 # Per-source extra flags.  The bf16 block kernel takes maxima of MFMA results
 # and masked scores, which are never NaN: without NaN semantics the compiler

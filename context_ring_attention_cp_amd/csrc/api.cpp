@@ -508,7 +508,8 @@ static cp_status rank_forward_impl(const cp_attn_desc* desc, const void* q, cons
                                    const void* const* v_blocks, void* out, float* m_out, float* l_out, float* lse_out,
                                    void* workspace, size_t workspace_bytes, void* compute_stream, void* copy_stream,
                                    int32_t flags, cp_attn_profiler* prof, bool fp8, const float* q_scale,
-                                   const float* const* k_scales, const float* const* v_scales) {
+                                   const float* const* k_scales, const float* const* v_scales,
+                                   bool static_ws = false) {
   g_last_error.clear();
   cp_status st = check_desc(desc);
   if (st != CP_OK) return st;
@@ -533,14 +534,27 @@ static cp_status rank_forward_impl(const cp_attn_desc* desc, const void* q, cons
       return st;
   }
   const WorkspaceLayout wl = layout_of(desc);
-  if (!workspace) return fail(CP_ERR_WORKSPACE, "workspace is NULL");
-  if (!aligned(workspace, 256)) return fail(CP_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-  if (workspace_bytes < wl.total)
-    return fail(CP_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, wl.total);
+  if (static_ws) {
+    if (wl.total > CP_STATIC_SCRATCH_BYTES)
+      return fail(CP_ERR_WORKSPACE,
+                  "this shard needs %zu bytes of scratch, more than the %zu of the static scratch "
+                  "(CP_STATIC_SCRATCH_BYTES): use cp_attn_rank_forward with a workspace",
+                  wl.total, (size_t)CP_STATIC_SCRATCH_BYTES);
+  } else {
+    if (!workspace) return fail(CP_ERR_WORKSPACE, "workspace is NULL");
+    if (!aligned(workspace, 256)) return fail(CP_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < wl.total)
+      return fail(CP_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, wl.total);
+  }
   const bool prefetch = flags & CP_RING_PREFETCH;
   if (prefetch && (copy_stream == compute_stream))
     return fail(CP_ERR_INVALID_ARG, "CP_RING_PREFETCH needs a copy_stream distinct from compute_stream");
   if (sched.empty()) return fail(CP_ERR_INVALID_ARG, "no visible block");   // unreachable: the diagonal is visible
+  if (static_ws) {
+    // every argument is valid: the first HIP call looks up this device's array
+    const hipError_t se = static_scratch(&workspace, &workspace_bytes);
+    if (se != hipSuccess) return hip_fail(se, "static scratch lookup");
+  }
 
   hipStream_t cs = (hipStream_t)compute_stream;
   hipStream_t xs = (hipStream_t)copy_stream;
@@ -646,6 +660,14 @@ cp_status cp_attn_rank_forward(const cp_attn_desc* desc, const void* q, const vo
                                int32_t flags, cp_attn_profiler* prof) {
   return rank_forward_impl(desc, q, k_blocks, v_blocks, out, m_out, l_out, lse_out, workspace, workspace_bytes,
                            compute_stream, copy_stream, flags, prof, false, nullptr, nullptr, nullptr);
+}
+
+cp_status cp_attn_rank_forward_static(const cp_attn_desc* desc, const void* q, const void* const* k_blocks,
+                                      const void* const* v_blocks, void* out, float* m_out, float* l_out,
+                                      float* lse_out, void* compute_stream, void* copy_stream, int32_t flags,
+                                      cp_attn_profiler* prof) {
+  return rank_forward_impl(desc, q, k_blocks, v_blocks, out, m_out, l_out, lse_out, nullptr, 0, compute_stream,
+                           copy_stream, flags, prof, false, nullptr, nullptr, nullptr, true);
 }
 
 cp_status cp_attn_rank_forward_fp8(const cp_attn_desc* desc, const void* q, const float* q_scale,

@@ -78,6 +78,10 @@ typedef enum {
 
 #define CP_MAX_RING 64      /* largest ring size N (and merge count n) accepted */
 
+/* Bytes of the static device scratch of cp_attn_rank_forward_static (64 MiB
+ * per GPU the library runs on, held until the process ends). */
+#define CP_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
 /* Problem description (the shard statement of the pages: Q_i, K_j, V_j of
  * shape (S/N) x H x d, rank i, ring size N, mask).  */
 typedef struct {
@@ -182,6 +186,25 @@ cp_status cp_attn_rank_forward(const cp_attn_desc* desc, const void* q,
                                void* out, float* m_out, float* l_out, float* lse_out,
                                void* workspace, size_t workspace_bytes, void* compute_stream,
                                void* copy_stream, int32_t flags, cp_attn_profiler* prof);
+
+/* For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid allocation): cp_attn_rank_forward
+ * with the same arguments except the workspace, which is a static device array
+ * of CP_STATIC_SCRATCH_BYTES inside the library (one per GPU, on the current
+ * device).  It runs the same kernels in the same order, so its results are
+ * bit-identical to cp_attn_rank_forward's.  It calls no allocation routine
+ * (only the per-call HIP events of the ring hand-offs are created and
+ * destroyed).  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind (no part of it needs clearing: the receive writes whole
+ * slots and the first step writes the running state), so calls that overlap
+ * on one GPU race: the caller runs them one after another.
+ * Errors: CP_ERR_WORKSPACE when cp_attn_workspace_bytes(desc) exceeds
+ * CP_STATIC_SCRATCH_BYTES (then nothing is enqueued); otherwise as
+ * cp_attn_rank_forward. */
+cp_status cp_attn_rank_forward_static(const cp_attn_desc* desc, const void* q,
+                                      const void* const* k_blocks, const void* const* v_blocks, void* out,
+                                      float* m_out, float* l_out, float* lse_out, void* compute_stream,
+                                      void* copy_stream, int32_t flags, cp_attn_profiler* prof);
 
 /* ---- All-to-all (Ulysses) context parallelism, one rank's share ----------
  * The second scheme of the compassingai.com page (section

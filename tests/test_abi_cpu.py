@@ -241,6 +241,33 @@ def test_rank_forward_argument_errors():
     assert st == B.CP_ERR_WORKSPACE
 
 
+def test_rank_forward_static_argument_errors():
+    """The allocation-free rank forward validates everything, the size of the
+    shard's scratch against CP_STATIC_SCRATCH_BYTES included, before its first
+    HIP call (these calls fail without a GPU)."""
+    lib = B.lib()
+    P = ctypes.c_void_p
+    blocks = (P * 4)(FAKE, FAKE + 256, FAKE + 512, FAKE + 768)
+    S1, S2 = 0x1000, 0x2000
+    d = _desc()
+    assert B.cp_attn_workspace_bytes(d) <= B.CP_STATIC_SCRATCH_BYTES
+    cases = [
+        ((d.ref, FAKE, blocks, blocks, FAKE, None, None, None, S1, S2, 8, None), B.CP_ERR_INVALID_ARG, "flags"),
+        ((d.ref, None, blocks, blocks, FAKE, None, None, None, S1, S2, 1, None), B.CP_ERR_INVALID_ARG, "q is NULL"),
+        ((d.ref, FAKE, blocks, blocks, FAKE, None, None, None, S1, S1, 1, None), B.CP_ERR_INVALID_ARG, "copy_stream"),
+    ]
+    # the largest bf16 shard that fits, and the next one that does not
+    small = _desc(L=4096, H=8)
+    big = _desc(L=8192, H=8)
+    assert B.cp_attn_workspace_bytes(small) <= B.CP_STATIC_SCRATCH_BYTES < B.cp_attn_workspace_bytes(big)
+    cases.append(((big.ref, FAKE, blocks, blocks, FAKE, None, None, None, S1, S2, 1, None), B.CP_ERR_WORKSPACE,
+                  "static scratch"))
+    for args, status, msg in cases:
+        st = _status(lib.cp_attn_rank_forward_static, *args)
+        assert st == status, (msg, st, B.last_error())
+        assert msg in B.last_error(), (msg, B.last_error())
+
+
 def test_host_query_argument_errors():
     lib = B.lib()
     d = _desc()
