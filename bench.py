@@ -31,6 +31,8 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 
 PEAK_FP8_TFLOPS = 5033.2      # MI355X dense FP8 MFMA: twice the bf16 rate (the published 5.0 PF)
 PEAK_HBM_GBS = 8000.0
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
+STREAM_KERNEL = "lds_stream_kernel"     # the global->LDS read of cp_attn_measure_lds_stream
+STREAM_MIB = 256
 _BLK = 32768 * 32 * 128                 # elements of one K or V block of the 128K example
 # Per profiled kernel: its name in the traces, the sources it is compiled
 # from, the committed PMC summary, the bytes of one ring-receive copy of the
@@ -40,10 +42,10 @@ KERNELS = {
     # block; <128, true>: V in the tiles the ring receive writes) share the prefix
     "bf16": dict(name="attn_block_bf16_kernel<128", srcs=("attn_mfma.hip", "gfx950_util.h", "kernels.h"),
                  json="attn_block_bf16__causal_128k_last_rank.traffic.json", copy_bytes=2 * _BLK,
-                 cmd="python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-secondary"),
+                 cmd="python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-secondary --calibration-read-mib 256"),
     "fp8": dict(name="attn_block_fp8_kernel<128", srcs=("attn_fp8.hip", "gfx950_util.h", "kernels.h"),
                 json="attn_block_fp8__causal_128k_last_rank.traffic.json", copy_bytes=_BLK,
-                cmd="python3 bench.py --fp8-only --steps 1 --warmup 0"),
+                cmd="python3 bench.py --fp8-only --steps 1 --warmup 0 --calibration-read-mib 256"),
 }
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", KERNELS["bf16"]["json"])
 
@@ -83,10 +85,21 @@ def summarize_pmc(fetch_dir: str, write_dir: str, which: str = "bf16", out: str 
         rows = _pmc_rows(d, counter)
         cal = [v for _, k, v in rows if COPY_KERNEL in k and abs(v * 1024 - copy_bytes) < 0.6 * copy_bytes]
         att = [v for _, k, v in rows if attn_kernel in k]
+        stream = [v for _, k, v in rows if STREAM_KERNEL in k]
         if not cal or not att:
             raise SystemExit(f"{counter}: calibration copies {len(cal)}, attention dispatches {len(att)}")
-        factor = copy_bytes / (sum(cal) / len(cal) * 1024)
-        res[name] = {"counter": counter, "kib_per_dispatch": att, "copy_kib": sum(cal) / len(cal), "factor": factor}
+        copy_factor = copy_bytes / (sum(cal) / len(cal) * 1024)
+        res[name] = {"counter": counter, "kib_per_dispatch": att, "copy_kib": sum(cal) / len(cal),
+                     "copy_factor": copy_factor}
+        if name == "fetch" and stream:
+            # bytes read through the same global->LDS fetch as the attention kernel's tiles
+            res[name]["stream_kib"] = stream[-1]
+            res[name]["stream_factor"] = (STREAM_MIB << 20) / (stream[-1] * 1024)
+            res[name]["factor"] = res[name]["stream_factor"]
+            res[name]["calibration"] = f"{STREAM_KERNEL}: global_load_lds_dwordx4 over {STREAM_MIB} MiB"
+        else:
+            res[name]["factor"] = copy_factor
+            res[name]["calibration"] = f"ring-receive copies ({COPY_KERNEL}) of {copy_bytes} bytes"
     n = min(len(res["fetch"]["kib_per_dispatch"]), len(res["write"]["kib_per_dispatch"]))
     per = [res["fetch"]["kib_per_dispatch"][i] * 1024 * res["fetch"]["factor"]
            + res["write"]["kib_per_dispatch"][i] * 1024 * res["write"]["factor"] for i in range(n)]
@@ -130,6 +143,11 @@ def parse():
                     help="the kernel --summarize-pmc summarises")
     ap.add_argument("--fp8-only", action="store_true",
                     help="time only the FP8 (e4m3) forward of the 128K last-rank shard and print its JSON")
+    ap.add_argument("--calibration-read-mib", type=int, default=0,
+                    help="after the timed steps, read this many MiB once through the global->LDS fetch "
+                         "(the HBM counter calibration of a --pmc run)")
+    ap.add_argument("--only", choices=SECONDARY, default=None,
+                    help="time only this secondary workload and print its JSON (for a profiler run)")
     return ap.parse_args()
 
 
@@ -165,6 +183,71 @@ def cpu_baseline(spec, q, k, v, rows_n: int):
             "sample": f"{rows_n} evenly spaced query rows of head 0 of {spec.H} ({pairs} visible pairs, "
                       f"{dt:.1f} s wall, fp64 numpy, materialised score rows)",
             "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def oracle_timing(seed: int, rows_n: int = 1024) -> dict:
+    """The fp64 oracle, as it is, timed on every workload: the tiny fp32 ring
+    whole (all 4 ranks), and for the others `rows_n` evenly spaced query rows
+    of the benchmarked rank against all its keys, on a one-head draw of the
+    same shapes (the oracle's cost per head does not depend on the values).
+    Reports the BLAS library and its threads, the sample's wall time and
+    rate on the causal-adjusted count, and the whole config's time
+    extrapolated from that rate (labelled as such)."""
+    import oracle
+    from harness.inputs import ShardSpec, make_inputs, standard_configs
+    blas = {}
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = {"library": info[0].get("internal_api"), "version": info[0].get("version"),
+                    "threads": info[0].get("num_threads"), "path": os.path.basename(info[0].get("filepath", ""))}
+    except Exception:  # noqa: BLE001
+        pass
+    res = {"blas": blas, "host_cpus": len(os.sched_getaffinity(0)), "configs": {}}
+    for cfg, full in standard_configs(seed).items():
+        spec1 = ShardSpec(S=full.S, N=full.N, H=1, d=full.d, dtype=full.dtype, mask=full.mask, rank=full.rank,
+                          B=full.B, cfg_id=full.cfg_id, q_scale=full.q_scale, cu_seqlens=full.cu_seqlens)
+        ranks = list(range(full.N)) if cfg == 1 else [full.rank]
+        inp = make_inputs(spec1, seed, ranks=ranks)
+        blocks = oracle.ring_schedule(full.N, full.rank, full.L, full.mask, full.cu_seqlens)
+        t0 = time.perf_counter()
+        pairs = 0
+        for r in ranks:
+            rows = (np.arange(full.L, dtype=np.int64) if cfg == 1
+                    else np.linspace(0, full.L - 1, min(rows_n, full.L)).astype(np.int64))
+            kb = {j: inp["k"][j] for j in range(full.N)} if cfg == 1 else {j: inp["k"][j] for j in blocks}
+            vb = {j: inp["v"][j] for j in range(full.N)} if cfg == 1 else {j: inp["v"][j] for j in blocks}
+            oracle.rank_attention(inp["q"][r], kb, vb, r, full.N, full.mask, full.cu_seqlens, rows=rows, heads=[0])
+            p = r * full.L + rows
+            if full.mask == "none":
+                pairs += len(rows) * full.S
+            else:
+                first = 0 if full.mask == "causal" else oracle.doc_start(p, full.cu_seqlens)
+                pairs += int(np.sum(p - first + 1))
+        dt = time.perf_counter() - t0
+        rate = 4.0 * full.d * pairs / dt
+        total_pairs = sum(oracle.visible_pairs(full.N, full.L, r, full.mask, full.cu_seqlens) for r in ranks)
+        res["configs"][f"cfg{cfg}"] = {
+            "workload": full.name,
+            "sample": ("all rows of the 4 ranks, one head of 2" if cfg == 1 else
+                       f"{len(rows)} evenly spaced rows of rank {full.rank}, one head of {full.H}"),
+            "sample_s": round(dt, 3), "gflops": round(rate / 1e9, 2),
+            "full_config_s_extrapolated": round(4.0 * full.d * total_pairs * full.H * full.B / rate, 1)}
+    return res
+
+
+def calibration_read(cp, mib: int, stream) -> None:
+    """Read `mib` MiB once through the global->LDS fetch (cp_attn_measure_lds_stream):
+    the HBM byte counters of a --pmc run are calibrated on this kernel."""
+    if not mib:
+        return
+    import torch
+    buf = torch.ones(mib << 18, device="cuda")     # MiB of float32
+    torch.cuda.synchronize()
+    cp.cp_attn_measure_lds_stream(buf, stream=stream)
+    torch.cuda.synchronize()
+    del buf
 
 
 def _timed(fn, stream, warmup: int, reps: int) -> float:
@@ -213,63 +296,107 @@ def _timed_flushed(fn, stream, warmup: int, reps: int, flush) -> dict:
     return {"median": float(np.median(t)), "mean": float(np.mean(t))}
 
 
-def secondary(seed: int, reps: int = 5):
+SECONDARY = ("cfg2", "cfg5", "cfg4", "ulysses", "fp8")
+
+
+def secondary(seed: int, reps: int = 5, only=None):
     """The other workloads of the path, timed briefly: the causal 32K
     last-rank shard, the packed-document shard (rank_forward, ring prefetch),
     the bidirectional 64K merge stress case (8 PARTIAL_LSE launches, then one
-    merge in a shuffled order; the merge is reported against HBM), and one
-    rank's share of all-to-all (Ulysses) context parallelism at 128K.  The
-    32K shard and the merge stress case fit in the caches, so they are timed
-    per iteration with the caches flushed in between (median of 10)."""
+    merge in a shuffled order; the merge is reported against HBM), one rank's
+    share of all-to-all (Ulysses) context parallelism at 128K and the FP8
+    forward.  The 32K shard and the merge stress case fit in the caches, so
+    they are timed per iteration with the caches flushed in between (median of
+    10).  `only` names one of SECONDARY to run alone (for a profiler run)."""
     import torch
 
     import context_ring_attention_cp_amd as cp
-    from harness.inputs import TENSOR_K, TENSOR_Q, TENSOR_V, bf16_bits, draw_shard, shuffled_order, standard_configs
-
-    def dev(x):
-        return torch.from_numpy(np.ascontiguousarray(bf16_bits(x)).view(np.int16)).view(torch.bfloat16).to("cuda")
+    from harness.inputs import standard_configs
 
     out = {}
     cfgs = standard_configs(seed)
     cs, xs = torch.cuda.Stream(), torch.cuda.Stream()
-    flush = torch.ones(128 << 20, device="cuda")         # 512 MiB, read between iterations of cfg 2 and 4
-    for cfg in (2, 5):
-        spec = cfgs[cfg]
-        cu_dev = None if spec.cu_seqlens is None else torch.from_numpy(spec.cu_seqlens).to("cuda")
-        desc = cp.Desc(spec.B, spec.H, spec.d, spec.N, spec.L, spec.rank, "bf16", spec.mask,
-                       cu_seqlens=spec.cu_seqlens, cu_seqlens_dev=cu_dev)
-        sched = cp.cp_attn_ring_schedule(desc, cp.CP_RING_PREFETCH)
-        q = dev(draw_shard(spec, seed, TENSOR_Q, spec.rank))
-        kb = [dev(draw_shard(spec, seed, TENSOR_K, j)) if j in sched else None for j in range(spec.N)]
-        vb = [dev(draw_shard(spec, seed, TENSOR_V, j)) if j in sched else None for j in range(spec.N)]
-        o = torch.empty((1, spec.L, spec.H, spec.d), dtype=torch.bfloat16, device="cuda")
-        lse = torch.empty((1, spec.H, spec.L), device="cuda")
-        ws = cp.alloc_workspace(desc)
-        run = lambda: cp.cp_attn_rank_forward(desc, q, kb, vb, o, None, None, lse, workspace=ws,  # noqa: E731
-                                              compute_stream=cs, copy_stream=xs, flags=cp.CP_RING_PREFETCH)
-        fl = attn_flops(spec, cp.cp_attn_visible_pairs(desc))
-        if cfg == 2:
-            # K/V of this shard (4 x 32 MiB) would stay in the caches between iterations
-            t = _timed_flushed(run, cs, 3, 10, flush)
-            ms = t["median"]
-            extra = {"ms_mean": round(t["mean"], 4), "timing": "median of 10, caches flushed between iterations"}
+    for name in SECONDARY:
+        if only is not None and name != only:
+            continue
+        if name in ("cfg2", "cfg5"):
+            out[name] = _sec_ring(cp, cfgs[int(name[3])], seed, cs, xs, reps)
+        elif name == "cfg4":
+            out[name] = _sec_merge(cp, cfgs[4], seed, cs)
+        elif name == "ulysses":
+            out[name] = _sec_ulysses(cp, cfgs[3], seed, cs, reps)
         else:
-            ms = _timed(run, cs, 2, reps)
-            extra = {}
-        out[f"cfg{cfg}"] = {"workload": spec.name, "blocks": sched, "ms": round(ms, 4),
-                            "tflops": round(fl / (ms * 1e-3) / 1e12, 2), **extra}
-        del q, kb, vb, o, lse, ws
-    spec = cfgs[4]
+            out[name] = fp8_forward(cp, cfgs[3], seed, cs, xs, reps)
+        torch.cuda.empty_cache()
+    return out
+
+
+def _dev_bf16(x):
+    import torch
+
+    from harness.inputs import bf16_bits
+    return torch.from_numpy(np.ascontiguousarray(bf16_bits(x)).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def _sec_ring(cp, spec, seed, cs, xs, reps):
+    """A rank forward with ring prefetch: the causal 32K last-rank shard (its
+    K/V would stay in the caches, so each iteration follows a 512 MiB cache
+    flush; median of 10) or the packed-document shard (mean of reps)."""
+    import torch
+
+    from harness.inputs import TENSOR_K, TENSOR_Q, TENSOR_V, draw_shard
+    cu_dev = None if spec.cu_seqlens is None else torch.from_numpy(spec.cu_seqlens).to("cuda")
+    desc = cp.Desc(spec.B, spec.H, spec.d, spec.N, spec.L, spec.rank, "bf16", spec.mask,
+                   cu_seqlens=spec.cu_seqlens, cu_seqlens_dev=cu_dev)
+    sched = cp.cp_attn_ring_schedule(desc, cp.CP_RING_PREFETCH)
+    q = _dev_bf16(draw_shard(spec, seed, TENSOR_Q, spec.rank))
+    kb = [_dev_bf16(draw_shard(spec, seed, TENSOR_K, j)) if j in sched else None for j in range(spec.N)]
+    vb = [_dev_bf16(draw_shard(spec, seed, TENSOR_V, j)) if j in sched else None for j in range(spec.N)]
+    o = torch.empty((1, spec.L, spec.H, spec.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((1, spec.H, spec.L), device="cuda")
+    ws = cp.alloc_workspace(desc)
+    run = lambda: cp.cp_attn_rank_forward(desc, q, kb, vb, o, None, None, lse, workspace=ws,  # noqa: E731
+                                          compute_stream=cs, copy_stream=xs, flags=cp.CP_RING_PREFETCH)
+    fl = attn_flops(spec, cp.cp_attn_visible_pairs(desc))
+    extra = {}
+    if spec.S <= 32768:
+        flush = torch.ones(128 << 20, device="cuda")     # 512 MiB
+        t = _timed_flushed(run, cs, 3, 10, flush)
+        ms = t["median"]
+        extra = {"ms_mean": round(t["mean"], 4), "timing": "median of 10, caches flushed between iterations"}
+        del flush
+    else:
+        ms = _timed(run, cs, 2, reps)
+    # per-launch attention kernel times of one more call
+    prof = cp.Profiler(len(sched))
+    cp.cp_attn_rank_forward(desc, q, kb, vb, o, None, None, lse, workspace=ws, compute_stream=cs,
+                            copy_stream=xs, flags=cp.CP_RING_PREFETCH, profiler=prof)
+    kms = prof.read()
+    prof.close()
+    return {"workload": spec.name, "blocks": sched, "ms": round(ms, 4),
+            "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+            "pct_of_peak": round(100.0 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "kernel_ms": [round(x, 4) for x in kms], **extra}
+
+
+def _sec_merge(cp, spec, seed, cs):
+    """Bidirectional 64K over 8 ranks, rank 5, Q x 3: eight PARTIAL_LSE
+    launches, then one merge in a seeded shuffled order (caches flushed by a
+    512 MiB read before each iteration; median of 10)."""
+    import torch
+
+    from harness.inputs import TENSOR_K, TENSOR_Q, TENSOR_V, draw_shard, shuffled_order
     desc = cp.Desc(spec.B, spec.H, spec.d, spec.N, spec.L, spec.rank, "bf16", spec.mask)
-    q = dev(draw_shard(spec, seed, TENSOR_Q, spec.rank))
-    kb = [dev(draw_shard(spec, seed, TENSOR_K, j)) for j in range(spec.N)]
-    vb = [dev(draw_shard(spec, seed, TENSOR_V, j)) for j in range(spec.N)]
+    q = _dev_bf16(draw_shard(spec, seed, TENSOR_Q, spec.rank))
+    kb = [_dev_bf16(draw_shard(spec, seed, TENSOR_K, j)) for j in range(spec.N)]
+    vb = [_dev_bf16(draw_shard(spec, seed, TENSOR_V, j)) for j in range(spec.N)]
     big, vec = (1, spec.L, spec.H, spec.d), (1, spec.H, spec.L)
     op = [torch.empty(big, device="cuda") for _ in range(spec.N)]
     lp = [torch.empty(vec, device="cuda") for _ in range(spec.N)]
     o = torch.empty(big, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(vec, device="cuda")
     order = shuffled_order(seed, 4, spec.N)
+    flush = torch.ones(128 << 20, device="cuda")
 
     def partials():
         with torch.cuda.stream(cs):
@@ -287,18 +414,20 @@ def secondary(seed: int, reps: int = 5):
     fl = attn_flops(spec, cp.cp_attn_visible_pairs(desc))
     rows = spec.L * spec.H
     merge_bytes = spec.N * rows * (spec.d * 4 + 4) + rows * (spec.d * 2 + 4)
-    out["cfg4"] = {"workload": spec.name, "order": order, "timing": "median of 10, caches flushed between iterations",
-                   "partials_ms_mean": round(tp["mean"], 4), "merge_ms_mean": round(tm["mean"], 4),
-                   "partials_ms": round(ms_p, 4),
-                   "partials_tflops": round(fl / (ms_p * 1e-3) / 1e12, 2), "merge_ms": round(ms_m, 4),
-                   "merge_algorithmic_bytes": merge_bytes,
-                   "merge_gbs": round(merge_bytes / (ms_m * 1e-3) / 1e9, 1),
-                   "merge_frac_of_hbm": round(merge_bytes / (ms_m * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    del q, kb, vb, op, lp, o, lse, flush
-    # All-to-all (Ulysses) share of the 128K example: rank 3 of 4 runs the
-    # whole sequence (S = 131072) on its 8 of 32 heads; the two all-to-alls are
-    # the regrouping copies.  Seeded N(0, 1) inputs drawn on the device.
-    spec = cfgs[3]
+    return {"workload": spec.name, "order": order, "timing": "median of 10, caches flushed between iterations",
+            "partials_ms_mean": round(tp["mean"], 4), "merge_ms_mean": round(tm["mean"], 4),
+            "partials_ms": round(ms_p, 4),
+            "partials_tflops": round(fl / (ms_p * 1e-3) / 1e12, 2), "merge_ms": round(ms_m, 4),
+            "merge_algorithmic_bytes": merge_bytes,
+            "merge_gbs": round(merge_bytes / (ms_m * 1e-3) / 1e9, 1),
+            "merge_frac_of_hbm": round(merge_bytes / (ms_m * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def _sec_ulysses(cp, spec, seed, cs, reps):
+    """All-to-all (Ulysses) share of the 128K example: rank 3 of 4 runs the
+    whole sequence (S = 131072) on its 8 of 32 heads; the two all-to-alls are
+    the regrouping copies.  Seeded N(0, 1) inputs drawn on the device."""
+    import torch
     gen = torch.Generator(device="cuda")
     gen.manual_seed(seed + 303)
     shape = (spec.B, spec.L, spec.H, spec.d)
@@ -313,12 +442,9 @@ def secondary(seed: int, reps: int = 5):
                 cs, 2, reps)
     fl = 4.0 * spec.d * hn * spec.B * spec.S * (spec.S + 1) / 2
     regroup = 8 * spec.B * spec.S * hn * spec.d * 2      # Q, K, V gathered and O scattered, each read + written
-    out["ulysses"] = {"workload": "all-to-all (Ulysses) share of the 128K example: rank 3 of 4, 8 of 32 heads "
-                                  "over S=131072, causal, bf16; the two all-to-alls simulated by regrouping copies",
-                      "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "regroup_bytes": regroup}
-    del qs, ks, vs, os_, ws, lse
-    out["fp8"] = fp8_forward(cp, spec, seed, cs, xs, reps)
-    return out
+    return {"workload": "all-to-all (Ulysses) share of the 128K example: rank 3 of 4, 8 of 32 heads "
+                        "over S=131072, causal, bf16; the two all-to-alls simulated by regrouping copies",
+            "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "regroup_bytes": regroup}
 
 
 def fp8_forward(cp, spec, seed: int, cs, xs, reps: int) -> dict:
@@ -431,10 +557,14 @@ def main():
     from harness.inputs import TENSOR_K, TENSOR_Q, TENSOR_V, bf16_bits, draw_shard, standard_configs
 
     cp.lib()
+    if args.only:
+        print(json.dumps(secondary(args.seed, max(args.steps, 1), only=args.only)[args.only]), flush=True)
+        return
     if args.fp8_only:
         cs, xs = torch.cuda.Stream(), torch.cuda.Stream()
         print(json.dumps(fp8_forward(cp, standard_configs(args.seed)[3], args.seed, cs, xs, max(args.steps, 1))),
               flush=True)
+        calibration_read(cp, args.calibration_read_mib, cs)
         return
     spec = standard_configs(args.seed)[3]
     N, L, H, d, r = spec.N, spec.L, spec.H, spec.d, spec.rank
@@ -486,6 +616,7 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
     step_ms = [e0.elapsed_time(marks[0])] + [marks[i - 1].elapsed_time(marks[i]) for i in range(1, args.steps)]
     kernel_ms = prof.read()
+    copy_ms = prof.read_copies()
     assert torch.isfinite(out.float()).all(), "non-finite output"
     value = flops / (ms_step * 1e-3) / 1e12
 
@@ -521,10 +652,20 @@ def main():
         "kernel_ms_per_step": [round(x, 4) for x in per_step[-1]] if per_step else [],
         "kernel_mean_ms": round(k_sum / max(1, len(kernel_ms)), 4),
         "ring_bytes_copied_per_step": 2 * blk_bytes * (len(sched) - 1),
+        # the simulated communication of each step (K copy + V re-layout on
+        # the copy stream, HIP events on that stream) against its computation
+        "comm": {"receive_ms_per_step": round(sum(copy_ms) / max(1, args.steps), 4),
+                 "receive_ms_each": [round(x, 4) for x in copy_ms[-(len(sched) - 1):]] if copy_ms else [],
+                 "attention_ms_per_step": round(k_sum / max(1, args.steps), 4),
+                 "comm_over_compute": round(sum(copy_ms) / k_sum, 4) if k_sum > 0 else None,
+                 "exposed_ms_per_step": round(ms_step - k_sum / max(1, args.steps), 4),
+                 "receive_gbs": round(2 * 2 * blk_bytes * len(copy_ms) / (sum(copy_ms) * 1e-3) / 1e9, 1)
+                 if copy_ms else None},
         "ring_traffic_formula_bytes": 2 * (2 * spec.B * spec.S * H * d * 2 // N) * (N - 1),
         "wall_s_timed": round(wall, 3),
     }
     prof.close()
+    calibration_read(cp, args.calibration_read_mib, cs)
     del m, lsum, ws
     if not args.no_secondary:
         log("[bench] backward of the same shard")
@@ -536,6 +677,8 @@ def main():
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows of head 0")
         res["cpu_baseline"] = cpu_baseline(spec, q, k, v, args.cpu_rows)
+        log("[bench] oracle timing of every workload")
+        res["cpu_baseline"]["per_config"] = oracle_timing(args.seed)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

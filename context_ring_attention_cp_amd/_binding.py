@@ -35,7 +35,8 @@ EXPORTED = [
     "cp_attn_profiler_destroy", "cp_attn_status_string", "cp_attn_last_error",
     "cp_attn_bwd_delta", "cp_attn_block_backward", "cp_attn_rank_backward",
     "cp_attn_ulysses_workspace_bytes", "cp_attn_ulysses_forward", "cp_attn_quantize_fp8",
-    "cp_attn_rank_forward_fp8", "cp_attn_rank_forward_static",
+    "cp_attn_rank_forward_fp8", "cp_attn_rank_forward_static", "cp_attn_profiler_read_copies",
+    "cp_attn_measure_lds_stream",
 ]
 
 
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.cp_attn_profiler_create.argtypes = [i32, ctypes.POINTER(vp)]
         L.cp_attn_profiler_reset.argtypes = [vp]
         L.cp_attn_profiler_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)]
+        L.cp_attn_profiler_read_copies.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)]
+        L.cp_attn_measure_lds_stream.argtypes = [vp, ctypes.c_size_t, vp]
         L.cp_attn_profiler_destroy.argtypes = [vp]
         L.cp_attn_profiler_destroy.restype = None
         L.cp_attn_bwd_delta.argtypes = [dp, vp, vp, f32p, vp]
@@ -313,6 +316,13 @@ def cp_attn_rank_forward_static(desc: Desc, q, k_blocks: Sequence, v_blocks: Seq
                                              profiler.handle if profiler is not None else None))
 
 
+def cp_attn_measure_lds_stream(src, stream=None) -> None:
+    """Read the bytes of the device tensor `src` once through the global -> LDS
+    fetch (a measurement helper: calibrates HBM byte counters)."""
+    nbytes = src.numel() * src.element_size()
+    _check(lib().cp_attn_measure_lds_stream(_ptr(src), nbytes, _stream(stream)))
+
+
 def cp_attn_ulysses_workspace_bytes(desc: Desc) -> int:
     n = int(lib().cp_attn_ulysses_workspace_bytes(desc.ref))
     if n == 0:
@@ -450,7 +460,7 @@ def cp_attn_visible_pairs(desc: Desc) -> int:
 
 
 class Profiler:
-    """Per-launch timer of cp_attn_rank_forward's attention kernels."""
+    """Per-launch timer of the rank forward's attention kernels and ring receives."""
 
     def __init__(self, capacity: int):
         h = ctypes.c_void_p(None)
@@ -465,6 +475,12 @@ class Profiler:
         buf = (ctypes.c_float * self.capacity)()
         cnt = ctypes.c_int32(0)
         _check(lib().cp_attn_profiler_read(self.handle, buf, self.capacity, ctypes.byref(cnt)))
+        return [float(buf[i]) for i in range(cnt.value)]
+
+    def read_copies(self):
+        buf = (ctypes.c_float * self.capacity)()
+        cnt = ctypes.c_int32(0)
+        _check(lib().cp_attn_profiler_read_copies(self.handle, buf, self.capacity, ctypes.byref(cnt)))
         return [float(buf[i]) for i in range(cnt.value)]
 
     def close(self) -> None:

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcpattn.so")
 
-SOURCES = ["api.cpp", "attn_mfma.hip", "attn_f32.hip", "merge_finalize.hip", "attn_bwd.hip", "ulysses.hip", "fp8.hip", "attn_fp8.hip", "v_tiles.hip", "scratch.hip"]
+SOURCES = ["api.cpp", "attn_mfma.hip", "attn_f32.hip", "merge_finalize.hip", "attn_bwd.hip", "ulysses.hip", "fp8.hip", "attn_fp8.hip", "v_tiles.hip", "scratch.hip", "measure.hip"]
 
 # Per-source extra flags.  The bf16 block kernel takes maxima of MFMA results
 # and masked scores, which are never NaN: without NaN semantics the compiler
@@ -28,6 +28,7 @@ SOURCES = ["api.cpp", "attn_mfma.hip", "attn_f32.hip", "merge_finalize.hip", "at
 # is inline assembly that sets M0 itself (the warning about clobbering the
 # reserved M0 is expected: nothing else in that kernel uses M0).
 EXTRA = {"attn_mfma.hip": ["-fno-honor-nans", "-Wno-inline-asm"], "attn_bwd.hip": ["-Wno-inline-asm"],
+         "measure.hip": ["-Wno-inline-asm"],
          "attn_fp8.hip": ["-fno-honor-nans", "-Wno-inline-asm"]}
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

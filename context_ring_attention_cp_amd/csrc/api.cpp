@@ -119,6 +119,24 @@ bool block_visible(const cp_attn_desc* d, int32_t j) {
   return first <= (int64_t)(j + 1) * d->L - 1;
 }
 
+// Rows of the shard that see block j.  Every row sees the rank's own block
+// and, under the causal or no mask, every visible block.  Under the document
+// mask, row p sees an earlier block j when its document starts at or before
+// the block's last key; the document start is non-decreasing in p, so those
+// rows are a prefix: the rows before the first document that starts after
+// the block (cu[ndocs] = N L always does).
+int64_t rows_seeing(const cp_attn_desc* d, int32_t j) {
+  if (d->mask != CP_MASK_DOC_CAUSAL || j >= d->rank) return d->L;
+  const int64_t last_key = (int64_t)(j + 1) * d->L - 1;
+  int lo = 0, hi = d->ndocs;
+  while (lo < hi) {
+    const int mid = (lo + hi) / 2;
+    if ((int64_t)d->cu_seqlens[mid] > last_key) hi = mid; else lo = mid + 1;
+  }
+  const int64_t r = (int64_t)d->cu_seqlens[lo] - (int64_t)d->rank * d->L;
+  return r < 0 ? 0 : (r > d->L ? d->L : r);
+}
+
 std::vector<int32_t> schedule(const cp_attn_desc* d, int32_t flags) {
   std::vector<int32_t> out;
   const int step = (flags & CP_RING_REVERSE) ? 1 : -1;
@@ -149,6 +167,8 @@ BlockArgs block_args(const cp_attn_desc* d, int32_t j, const void* q, const void
   a.ndocs = d->ndocs;
   a.cu = d->mask == CP_MASK_DOC_CAUSAL ? d->cu_seqlens_dev : nullptr;
   a.scale_log2 = scale_log2(d);
+  a.rows_end = d->L;
+  a.final_from = 0;
   return a;
 }
 
@@ -189,8 +209,9 @@ WorkspaceLayout layout_of(const cp_attn_desc* d) {
 }  // namespace
 
 struct cp_attn_profiler {
-  std::vector<hipEvent_t> start, stop;
-  int32_t used = 0;
+  std::vector<hipEvent_t> start, stop;            // attention launches
+  std::vector<hipEvent_t> copy_start, copy_stop;  // ring receives
+  int32_t used = 0, copies = 0;
 };
 
 extern "C" {
@@ -569,9 +590,11 @@ static cp_status rank_forward_impl(const cp_attn_desc* desc, const void* q, cons
   // ready[t]: block of step t is in its slot; done[t]: step t's kernel finished with its slot
   std::vector<hipEvent_t> ready(nsteps, nullptr), done(nsteps, nullptr);
   hipError_t e = hipSuccess;
+  hipEvent_t start_ev = nullptr;   // the copy stream's start (inputs ready), with prefetch
   auto cleanup = [&]() {
     for (auto ev : ready) if (ev) (void)hipEventDestroy(ev);
     for (auto ev : done) if (ev) (void)hipEventDestroy(ev);
+    if (start_ev) (void)hipEventDestroy(start_ev);
   };
   if (prefetch) {
     for (int32_t t = 0; t < nsteps; ++t) {
@@ -586,27 +609,41 @@ static cp_status rank_forward_impl(const cp_attn_desc* desc, const void* q, cons
   auto slot_v = [&](int32_t t) { return (void*)(ws + wl.slot_v[t & 1]); };
   auto enqueue_copy = [&](int32_t t, hipStream_t s) -> hipError_t {
     const int32_t j = sched[t];
-    hipError_t r = hipMemcpyAsync(slot_k(t), k_blocks[j], blk_bytes, hipMemcpyDeviceToDevice, s);
+    const bool timed = prof && prof->copies < (int32_t)prof->copy_start.size();
+    hipError_t r;
+    if (timed && (r = hipEventRecord(prof->copy_start[prof->copies], s)) != hipSuccess) return r;
+    r = hipMemcpyAsync(slot_k(t), k_blocks[j], blk_bytes, hipMemcpyDeviceToDevice, s);
     if (r != hipSuccess) return r;
-    if (v_tiled && fp8) return launch_v_tiles_fp8(v_blocks[j], slot_v(t), desc->L, desc->B, desc->H, desc->d, s);
-    if (v_tiled) return launch_v_tiles(v_blocks[j], slot_v(t), desc->L, desc->B, desc->H, desc->d, s);
-    return hipMemcpyAsync(slot_v(t), v_blocks[j], blk_bytes, hipMemcpyDeviceToDevice, s);
+    if (v_tiled && fp8) r = launch_v_tiles_fp8(v_blocks[j], slot_v(t), desc->L, desc->B, desc->H, desc->d, s);
+    else if (v_tiled) r = launch_v_tiles(v_blocks[j], slot_v(t), desc->L, desc->B, desc->H, desc->d, s);
+    else r = hipMemcpyAsync(slot_v(t), v_blocks[j], blk_bytes, hipMemcpyDeviceToDevice, s);
+    if (r != hipSuccess) return r;
+    if (timed) {
+      if ((r = hipEventRecord(prof->copy_stop[prof->copies], s)) != hipSuccess) return r;
+      prof->copies++;
+    }
+    return hipSuccess;
   };
-  // the copy stream starts after everything already queued on the compute stream (inputs ready)
-  hipEvent_t start_ev = nullptr;
+  // The copy stream starts after everything already queued on the compute
+  // stream (the inputs are ready), but not after the first attention kernel,
+  // which reads the rank's own block; that kernel is enqueued before the
+  // first receive, so the compute stream does not wait on the host's
+  // enqueueing of the copy.
   if (prefetch && nsteps > 1) {
     if ((e = hipEventCreateWithFlags(&start_ev, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventRecord(start_ev, cs)) != hipSuccess || (e = hipStreamWaitEvent(xs, start_ev, 0)) != hipSuccess) {
-      if (start_ev) (void)hipEventDestroy(start_ev);
+        (e = hipEventRecord(start_ev, cs)) != hipSuccess) {
       cleanup();
       return hip_fail(e, "copy stream start");
     }
-    (void)hipEventDestroy(start_ev);
-    if ((e = enqueue_copy(1, xs)) != hipSuccess || (e = hipEventRecord(ready[1], xs)) != hipSuccess) {
-      cleanup();
-      return hip_fail(e, "ring receive copy");
-    }
   }
+  auto start_copies = [&]() -> hipError_t {
+    hipError_t r = hipStreamWaitEvent(xs, start_ev, 0);
+    (void)hipEventDestroy(start_ev);
+    start_ev = nullptr;
+    if (r != hipSuccess) return r;
+    if ((r = enqueue_copy(1, xs)) != hipSuccess) return r;
+    return hipEventRecord(ready[1], xs);
+  };
 
   for (int32_t t = 0; t < nsteps; ++t) {
     const int32_t j = sched[t];
@@ -623,9 +660,17 @@ static cp_status rank_forward_impl(const cp_attn_desc* desc, const void* q, cons
       a.k_scale = k_scales[j];
       a.v_scale = v_scales[j];
     }
-    const bool last = t == nsteps - 1;
-    a.flags = (t > 0 ? F_READ_STATE : 0) | (last ? F_WRITE_FINAL : F_WRITE_STATE) |
-              (t > 0 && v_tiled ? F_V_TILED : 0);
+    // Mask-aware rows: this step runs the rows that see block j only, and a
+    // row that sees no later block of the schedule stores its final output
+    // here (those are the rows from final_from on; the others keep the state)
+    a.rows_end = rows_seeing(desc, j);
+    int64_t later = 0;
+    for (int32_t u = t + 1; u < nsteps; ++u) {
+      const int64_t r = rows_seeing(desc, sched[u]);
+      if (r > later) later = r;
+    }
+    a.final_from = later;
+    a.flags = (t > 0 ? F_READ_STATE : 0) | F_WRITE_STATE | F_WRITE_FINAL | (t > 0 && v_tiled ? F_V_TILED : 0);
     a.st_o = (float*)(ws + wl.st_o);
     a.st_m = (float*)(ws + wl.st_m);
     a.st_l = (float*)(ws + wl.st_l);
@@ -641,6 +686,7 @@ static cp_status rank_forward_impl(const cp_attn_desc* desc, const void* q, cons
       if ((e = hipEventRecord(prof->stop[prof->used], cs)) != hipSuccess) { cleanup(); return hip_fail(e, "profiler record"); }
       prof->used++;
     }
+    if (t == 0 && start_ev && (e = start_copies()) != hipSuccess) { cleanup(); return hip_fail(e, "ring receive copy"); }
     if (prefetch && t + 1 < nsteps - 1) {
       // the receive for step t+2 reuses the slot of step t: wait for this kernel
       if ((e = hipEventRecord(done[t], cs)) != hipSuccess || (e = hipStreamWaitEvent(xs, done[t], 0)) != hipSuccess ||
@@ -680,6 +726,17 @@ cp_status cp_attn_rank_forward_fp8(const cp_attn_desc* desc, const void* q, cons
                            compute_stream, copy_stream, flags, prof, true, q_scale, k_scales, v_scales);
 }
 
+cp_status cp_attn_measure_lds_stream(const void* src, size_t bytes, void* stream) {
+  g_last_error.clear();
+  cp_status st = check_tensor(src, "src");
+  if (st != CP_OK) return st;
+  if (bytes == 0 || bytes % 4096 != 0 || bytes > ((size_t)1 << 46))
+    return fail(CP_ERR_INVALID_ARG, "bytes=%zu must be a positive multiple of 4096", bytes);
+  const hipError_t e = launch_lds_stream(src, (int64_t)bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "measurement kernel launch");
+  return CP_OK;
+}
+
 cp_status cp_attn_profiler_create(int32_t capacity, cp_attn_profiler** out) {
   g_last_error.clear();
   if (!out) return fail(CP_ERR_INVALID_ARG, "out is NULL");
@@ -688,9 +745,13 @@ cp_status cp_attn_profiler_create(int32_t capacity, cp_attn_profiler** out) {
   if (!p) return fail(CP_ERR_INVALID_ARG, "out of host memory");
   p->start.assign(capacity, nullptr);
   p->stop.assign(capacity, nullptr);
+  p->copy_start.assign(capacity, nullptr);
+  p->copy_stop.assign(capacity, nullptr);
   for (int32_t i = 0; i < capacity; ++i) {
     hipError_t e = hipEventCreate(&p->start[i]);
     if (e == hipSuccess) e = hipEventCreate(&p->stop[i]);
+    if (e == hipSuccess) e = hipEventCreate(&p->copy_start[i]);
+    if (e == hipSuccess) e = hipEventCreate(&p->copy_stop[i]);
     if (e != hipSuccess) {
       cp_attn_profiler_destroy(p);
       return hip_fail(e, "hipEventCreate");
@@ -704,6 +765,7 @@ cp_status cp_attn_profiler_reset(cp_attn_profiler* prof) {
   g_last_error.clear();
   if (!prof) return fail(CP_ERR_INVALID_ARG, "prof is NULL");
   prof->used = 0;
+  prof->copies = 0;
   return CP_OK;
 }
 
@@ -721,10 +783,26 @@ cp_status cp_attn_profiler_read(cp_attn_profiler* prof, float* ms_out, int32_t c
   return CP_OK;
 }
 
+cp_status cp_attn_profiler_read_copies(cp_attn_profiler* prof, float* ms_out, int32_t capacity, int32_t* count_out) {
+  g_last_error.clear();
+  if (!prof || !count_out) return fail(CP_ERR_INVALID_ARG, "prof/count_out is NULL");
+  if (capacity < prof->copies || (!ms_out && prof->copies > 0))
+    return fail(CP_ERR_INVALID_ARG, "capacity %d < %d recorded receives", capacity, prof->copies);
+  for (int32_t i = 0; i < prof->copies; ++i) {
+    hipError_t e = hipEventSynchronize(prof->copy_stop[i]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms_out[i], prof->copy_start[i], prof->copy_stop[i]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+  }
+  *count_out = prof->copies;
+  return CP_OK;
+}
+
 void cp_attn_profiler_destroy(cp_attn_profiler* prof) {
   if (!prof) return;
   for (auto ev : prof->start) if (ev) (void)hipEventDestroy(ev);
   for (auto ev : prof->stop) if (ev) (void)hipEventDestroy(ev);
+  for (auto ev : prof->copy_start) if (ev) (void)hipEventDestroy(ev);
+  for (auto ev : prof->copy_stop) if (ev) (void)hipEventDestroy(ev);
   delete prof;
 }
 

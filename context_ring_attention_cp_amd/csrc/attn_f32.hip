@@ -41,7 +41,8 @@ __global__ __launch_bounds__(kThreads) void attn_block_f32_kernel(BlockArgs a) {
   const int x4 = tid & (kLanesPerRow - 1);
   const int64_t L = a.L;
   const int H = a.H;
-  const int nqt = (int)((L + kRows - 1) / kRows);
+  const int64_t rows_end = a.rows_end;                     // rows taking part in this launch
+  const int nqt = (int)((rows_end + kRows - 1) / kRows);
   const int64_t hb = blockIdx.x / nqt;
   const int qt = nqt - 1 - (int)(blockIdx.x % nqt);
   const int h = (int)(hb % H), b = (int)(hb / H);
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_f32_kernel(BlockArgs a) {
   const int64_t p = a.q_pos0 + row;
   const int mask = a.mask;
   const bool doc = mask == MASK_DOC_CAUSAL;
-  const int64_t last = (q0 + kRows < L ? q0 + kRows : L) - 1;
+  const int64_t last = (q0 + kRows < rows_end ? q0 + kRows : rows_end) - 1;
 
   const int nkt = (int)((L + kKeys - 1) / kKeys);
   int kt_begin = 0, kt_end = nkt;
@@ -70,7 +71,8 @@ __global__ __launch_bounds__(kThreads) void attn_block_f32_kernel(BlockArgs a) {
     }
   }
   const bool rd = a.flags & F_READ_STATE;
-  if (kt_begin >= kt_end && rd && !(a.flags & (F_WRITE_FINAL | F_WRITE_PARTIAL))) return;
+  // nothing to compute and nothing to store: the state of these rows stays as it is
+  if (kt_begin >= kt_end && rd && !writes_final(a.flags, last, a.final_from) && !(a.flags & F_WRITE_PARTIAL)) return;
   const int64_t dstart = doc ? doc_start_of(a.cu, a.ndocs, row_ok ? p : a.q_pos0 + last) : 0;
 
   float q[DQ], o[DQ];
@@ -134,9 +136,9 @@ __global__ __launch_bounds__(kThreads) void attn_block_f32_kernel(BlockArgs a) {
     }
   }
 
-  if (!row_ok) return;
+  if (!row_ok || row >= rows_end) return;
   const bool has = l_run > 0.f;
-  if (a.flags & F_WRITE_STATE) {
+  if (writes_state(a.flags, row, a.final_from)) {
 #pragma unroll
     for (int x = 0; x < DQ; ++x) a.st_o[st_row + kLanesPerRow * x + x4] = o[x];
     if (x4 == 0) {
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_f32_kernel(BlockArgs a) {
   const float inv = has ? 1.f / l_run : 0.f;
   // v_log_f32 is the base-2 logarithm
   const float lse = has ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : -INFINITY;
-  if (a.flags & F_WRITE_FINAL) {
+  if (writes_final(a.flags, row, a.final_from)) {
     float* outp = (float*)a.out + st_row;
 #pragma unroll
     for (int x = 0; x < DQ; ++x) outp[kLanesPerRow * x + x4] = o[x] * inv;
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_f32_kernel(BlockArgs a) {
 }  // namespace
 
 hipError_t launch_block_f32(const BlockArgs& a, int d, hipStream_t s) {
-  const int64_t nqt = (a.L + kRows - 1) / kRows;
+  const int64_t nqt = (a.rows_end + kRows - 1) / kRows;
   const int64_t nwg = nqt * a.H * a.B;
   if (d == 128) attn_block_f32_kernel<128><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
   else attn_block_f32_kernel<64><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);

@@ -101,7 +101,8 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
   const int64_t L = a.L;
   const int H = a.H;
 
-  const int nqt = (int)((L + BM - 1) / BM);
+  const int64_t rows_end = a.rows_end;                     // rows taking part in this launch
+  const int nqt = (int)((rows_end + BM - 1) / BM);
   const int64_t nwg = (int64_t)nqt * H * a.B;
   const int64_t bid = blockIdx.x;
   const int64_t logical = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
   const int nkt = (int)((L + BN - 1) / BN);
   int kt_begin = 0, kt_end = nkt;
   {
-    const int64_t wg_last = (q0 + BM < L ? q0 + BM : L) - 1;
+    const int64_t wg_last = (q0 + BM < rows_end ? q0 + BM : rows_end) - 1;
     if (mask != MASK_NONE) {
       const int64_t hi = a.q_pos0 + wg_last - a.k_pos0;
       kt_end = hi < 0 ? 0 : (int)(hi / BN + 1 < nkt ? hi / BN + 1 : nkt);
@@ -142,7 +143,9 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
     }
   }
   const bool rd = a.flags & F_READ_STATE;
-  if (kt_begin >= kt_end && rd && !(a.flags & (F_WRITE_FINAL | F_WRITE_PARTIAL))) return;
+  // nothing to compute and nothing to store: the state of these rows stays as it is
+  const bool wg_final = writes_final(a.flags, (q0 + BM < rows_end ? q0 + BM : rows_end) - 1, a.final_from);
+  if (kt_begin >= kt_end && rd && !wg_final && !(a.flags & F_WRITE_PARTIAL)) return;
 
   const int64_t w_first = q0 + 32 * w;
   const bool wave_ok = w_first < L;
@@ -448,12 +451,12 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
     for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
   }
 
-  if (!row_ok) return;
+  if (!row_ok || qrow >= rows_end) return;
   const float l_tot = lacc[0];
   const bool has = l_tot > 0.f;
   const float m_run = m_true;
   // m in natural-log units of the true scores (c2 includes the FP8 scales)
-  if (a.flags & F_WRITE_STATE) {
+  if (writes_state(a.flags, qrow, a.final_from)) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -467,7 +470,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
   }
   const float inv = has ? 1.f / l_tot : 0.f;
   const float lse = has ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-  if (a.flags & F_WRITE_FINAL) {
+  if (writes_final(a.flags, qrow, a.final_from)) {
     bf16* outp = (bf16*)a.out + st_row;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -498,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
 }  // namespace
 
 hipError_t launch_block_fp8(const BlockArgs& a, int d, hipStream_t s) {
-  const int64_t nqt = (a.L + BM - 1) / BM;
+  const int64_t nqt = (a.rows_end + BM - 1) / BM;
   const int64_t nwg = nqt * a.H * a.B;
   const bool vt = (a.flags & F_V_TILED) != 0;
   if (d == 128) {

@@ -95,7 +95,8 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   // 8 XCDs round robin; the remap gives each XCD a contiguous run of logical
   // ids (one head's query tiles share its K/V in that XCD's L2).  Within a
   // head, the query tiles that see the most keys start first.
-  const int nqt = (int)((L + BM - 1) / BM);
+  const int64_t rows_end = a.rows_end;                     // rows taking part in this launch
+  const int nqt = (int)((rows_end + BM - 1) / BM);
   const int64_t nwg = (int64_t)nqt * H * a.B;
   const int64_t bid = blockIdx.x;
   const int64_t logical = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   const int nkt = (int)((L + BN - 1) / BN);
   int kt_begin = 0, kt_end = nkt;
   {
-    const int64_t wg_last = (q0 + BM < L ? q0 + BM : L) - 1;
+    const int64_t wg_last = (q0 + BM < rows_end ? q0 + BM : rows_end) - 1;
     if (mask != MASK_NONE) {
       const int64_t hi = a.q_pos0 + wg_last - a.k_pos0;   // last visible key (local)
       kt_end = hi < 0 ? 0 : (int)(hi / BN + 1 < nkt ? hi / BN + 1 : nkt);
@@ -133,7 +134,9 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
     }
   }
   const bool rd = a.flags & F_READ_STATE;
-  if (kt_begin >= kt_end && rd && !(a.flags & (F_WRITE_FINAL | F_WRITE_PARTIAL))) return;
+  // nothing to compute and nothing to store: the state of these rows stays as it is
+  const bool wg_final = writes_final(a.flags, (q0 + BM < rows_end ? q0 + BM : rows_end) - 1, a.final_from);
+  if (kt_begin >= kt_end && rd && !wg_final && !(a.flags & F_WRITE_PARTIAL)) return;
 
   // This wave's rows.  Every wave runs every key tile of the workgroup; tiles
   // a wave cannot see are fully masked (only the few tiles of a causal
@@ -458,12 +461,12 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
     for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
   }
 
-  if (!row_ok) return;
+  if (!row_ok || qrow >= rows_end) return;
   const float l_tot = l_run + xor32(l_run);
   const bool has = l_tot > 0.f;
   const float m_run = m_true;
 
-  if (a.flags & F_WRITE_STATE) {
+  if (writes_state(a.flags, qrow, a.final_from)) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -478,7 +481,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   const float inv = has ? 1.f / l_tot : 0.f;
   // v_log_f32 is the base-2 logarithm
   const float lse = has ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-  if (a.flags & F_WRITE_FINAL) {
+  if (writes_final(a.flags, qrow, a.final_from)) {
     bf16* outp = (bf16*)a.out + st_row;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -509,7 +512,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
 }  // namespace
 
 hipError_t launch_block_bf16(const BlockArgs& a, int d, hipStream_t s) {
-  const int64_t nqt = (a.L + BM - 1) / BM;
+  const int64_t nqt = (a.rows_end + BM - 1) / BM;
   const int64_t nwg = nqt * a.H * a.B;
   const bool vt = (a.flags & F_V_TILED) != 0;
   if (d == 128) {

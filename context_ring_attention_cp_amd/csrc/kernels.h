@@ -17,6 +17,13 @@ enum : int32_t {
                         // e4m3 [B, H, T8, d, 128] with the operand key order (launch_v_tiles_fp8)
 };
 
+// Per-row store decisions of a block launch (see BlockArgs::final_from).
+__host__ __device__ inline bool writes_final(int32_t flags, int64_t row, int64_t final_from) {
+  return (flags & F_WRITE_FINAL) && (!(flags & F_WRITE_STATE) || row >= final_from);
+}
+__host__ __device__ inline bool writes_state(int32_t flags, int64_t row, int64_t final_from) {
+  return (flags & F_WRITE_STATE) && (!(flags & F_WRITE_FINAL) || row < final_from);
+}
 // Keys of a tiled V block: L rounded up to whole 64-key tiles (T = that / 64).
 __host__ __device__ inline int64_t v_tiled_keys(int64_t L) { return (L + 63) / 64 * 64; }
 
@@ -36,6 +43,12 @@ struct BlockArgs {
   const int32_t* cu;     // device cu_seqlens (DOC_CAUSAL)
   float scale_log2;      // softmax scale * log2(e)
   int32_t flags;
+  // Rows of this launch: query rows [0, rows_end) take part (the grid covers
+  // their tiles only).  When both F_WRITE_STATE and F_WRITE_FINAL are set,
+  // rows [final_from, rows_end) store the final output and the rows before
+  // them the running state; with one of the two flags every row stores that.
+  int64_t rows_end;
+  int64_t final_from;
   // running state
   float* st_o;           // [B, L, H, d]
   float* st_m;           // [B, H, L] natural-log units

@@ -27,6 +27,9 @@ hipError_t launch_a2a_gather_v_tiles(const RegroupArgs& a, hipStream_t s);
 hipError_t launch_quantize_fp8(const QuantArgs& a, int d, hipStream_t s);
 // FP8 (e4m3) inputs, bf16 output; the same flags and state as the bf16 kernel.
 hipError_t launch_block_fp8(const BlockArgs& a, int d, hipStream_t s);
+// Measurement: read `bytes` (a multiple of 4096) from src through the
+// global -> LDS fetch once, discarding them (measure.hip).
+hipError_t launch_lds_stream(const void* src, int64_t bytes, hipStream_t s);
 // Device address and size of the static scratch on the current device
 // (looked up once per device; scratch.hip).
 hipError_t static_scratch(void** addr, size_t* bytes);

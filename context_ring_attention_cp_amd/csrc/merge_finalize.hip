@@ -50,31 +50,65 @@ constexpr int kBatch = 8;
 // grid: one workgroup per kThreads / (D / 8) consecutive (batch, row, head)
 // triples.  Each thread owns 8 consecutive head-dim elements (two 16-byte
 // loads per part), so a thread keeps 2 kBatch partial loads in flight.
-template <int D>
+template <int D, bool I32>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   constexpr int D8 = D / 8;                       // threads per row-head
   constexpr int RPW = kThreads / D8;              // row-heads per workgroup
   const int64_t rowhead = (int64_t)blockIdx.x * RPW + threadIdx.x / D8;   // ((b L) + row) H + h
   if (rowhead >= (int64_t)a.B * a.L * a.H) return;
-  const int h = (int)(rowhead % a.H);
-  const int64_t bl = rowhead / a.H;
-  const int64_t row = bl % a.L, b = bl / a.L;
+  int64_t h, row, b;
+  if constexpr (I32) {        // 32-bit divisions when B L H fits (the usual case)
+    const uint32_t rh = (uint32_t)rowhead, bl = rh / (uint32_t)a.H;
+    h = rh - bl * (uint32_t)a.H;
+    b = bl / (uint32_t)a.L;
+    row = bl - (uint32_t)b * (uint32_t)a.L;
+  } else {
+    h = rowhead % a.H;
+    const int64_t bl = rowhead / a.H;
+    row = bl % a.L;
+    b = bl / a.L;
+  }
   const int x8 = threadIdx.x % D8;
   const int64_t ml = (b * a.H + h) * a.L + row;
   const int64_t off = rowhead * D + 8 * x8;
   const int n = a.n;
 
-  // lse = ln sum exp(lse_j), in base 2 with the max factored out
+  // The partials of the first kBatch parts are requested before the lse
+  // values, so the two memory latencies of a thread overlap.
+  float4 v0[kBatch], v1[kBatch];
+#pragma unroll
+  for (int t = 0; t < kBatch; ++t) {
+    v0[t] = t < n ? *(const float4*)(a.o[t] + off) : float4{0.f, 0.f, 0.f, 0.f};
+    v1[t] = t < n ? *(const float4*)(a.o[t] + off + 4) : float4{0.f, 0.f, 0.f, 0.f};
+  }
+  // lse = ln sum exp(lse_j), in base 2 with the max factored out.  The lse
+  // values held in registers are loaded without a branch (slots from n on
+  // alias part 0, so every load is valid) and the unused ones masked after.
   float l2[kRegParts];
+#pragma unroll
+  for (int j = 0; j < kRegParts; ++j) l2[j] = a.lse[j][ml];
   float mx = -INFINITY;
 #pragma unroll
   for (int j = 0; j < kRegParts; ++j) {
-    l2[j] = j < n ? a.lse[j][ml] * kLog2e : -INFINITY;
+    l2[j] = j < n ? l2[j] * kLog2e : -INFINITY;
     mx = fmaxf(mx, l2[j]);
   }
   for (int j = kRegParts; j < n; ++j) mx = fmaxf(mx, a.lse[j][ml] * kLog2e);
   float4 o0 = float4{0.f, 0.f, 0.f, 0.f}, o1 = o0;
   float lse = -INFINITY;
+  auto fma_batch = [&](const float (&wj)[kBatch]) {
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) {
+      o0.x = __builtin_fmaf(wj[t], v0[t].x, o0.x);
+      o0.y = __builtin_fmaf(wj[t], v0[t].y, o0.y);
+      o0.z = __builtin_fmaf(wj[t], v0[t].z, o0.z);
+      o0.w = __builtin_fmaf(wj[t], v0[t].w, o0.w);
+      o1.x = __builtin_fmaf(wj[t], v1[t].x, o1.x);
+      o1.y = __builtin_fmaf(wj[t], v1[t].y, o1.y);
+      o1.z = __builtin_fmaf(wj[t], v1[t].z, o1.z);
+      o1.w = __builtin_fmaf(wj[t], v1[t].w, o1.w);
+    }
+  };
   if (mx != -INFINITY) {
     float tot = 0.f;
 #pragma unroll
@@ -82,33 +116,33 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     for (int j = kRegParts; j < n; ++j) tot += __builtin_amdgcn_exp2f(__builtin_fmaf(a.lse[j][ml], kLog2e, -mx));
     const float lse2 = mx + __builtin_amdgcn_logf(tot);   // v_log_f32 is log2
     lse = lse2 * kLn2;
-    // terms in the given order, 2 kBatch partial loads in flight at a time
-    for (int j0 = 0; j0 < n; j0 += kBatch) {
-      float4 v0[kBatch], v1[kBatch];
-      float wj[kBatch];
+    // terms in the given order; the weights of the parts held in registers
+    // are indexed at compile time
+    float wj[kBatch];
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) wj[t] = t < n ? __builtin_amdgcn_exp2f(l2[t] - lse2) : 0.f;
+    fma_batch(wj);
+    static_assert(kRegParts == 2 * kBatch, "two batches held in registers");
+    if (n > kBatch) {
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) {
+        const int j = kBatch + t;
+        v0[t] = j < n ? *(const float4*)(a.o[j] + off) : float4{0.f, 0.f, 0.f, 0.f};
+        v1[t] = j < n ? *(const float4*)(a.o[j] + off + 4) : float4{0.f, 0.f, 0.f, 0.f};
+        wj[t] = j < n ? __builtin_amdgcn_exp2f(l2[j] - lse2) : 0.f;
+      }
+      fma_batch(wj);
+    }
+    // parts from kRegParts on: their lse values are read again
+    for (int j0 = kRegParts; j0 < n; j0 += kBatch) {
 #pragma unroll
       for (int t = 0; t < kBatch; ++t) {
         const int j = j0 + t;
         v0[t] = j < n ? *(const float4*)(a.o[j] + off) : float4{0.f, 0.f, 0.f, 0.f};
         v1[t] = j < n ? *(const float4*)(a.o[j] + off + 4) : float4{0.f, 0.f, 0.f, 0.f};
+        wj[t] = j < n ? __builtin_amdgcn_exp2f(__builtin_fmaf(a.lse[j][ml], kLog2e, -lse2)) : 0.f;
       }
-#pragma unroll
-      for (int t = 0; t < kBatch; ++t) {
-        const int j = j0 + t;
-        const float lj = j < kRegParts ? l2[j < kRegParts ? j : 0] : (j < n ? a.lse[j][ml] * kLog2e : -INFINITY);
-        wj[t] = j < n ? __builtin_amdgcn_exp2f(lj - lse2) : 0.f;
-      }
-#pragma unroll
-      for (int t = 0; t < kBatch; ++t) {
-        o0.x = __builtin_fmaf(wj[t], v0[t].x, o0.x);
-        o0.y = __builtin_fmaf(wj[t], v0[t].y, o0.y);
-        o0.z = __builtin_fmaf(wj[t], v0[t].z, o0.z);
-        o0.w = __builtin_fmaf(wj[t], v0[t].w, o0.w);
-        o1.x = __builtin_fmaf(wj[t], v1[t].x, o1.x);
-        o1.y = __builtin_fmaf(wj[t], v1[t].y, o1.y);
-        o1.z = __builtin_fmaf(wj[t], v1[t].z, o1.z);
-        o1.w = __builtin_fmaf(wj[t], v1[t].w, o1.w);
-      }
+      fma_batch(wj);
     }
   }
   store4(a.out, off, a.out_bf16, o0);
@@ -149,8 +183,14 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalizeArgs a) {
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   const int rpw = kThreads / (a.d / 8);
   const dim3 grid((unsigned)(((int64_t)a.B * a.L * a.H + rpw - 1) / rpw));
-  if (a.d == 128) merge_kernel<128><<<grid, dim3(kThreads), 0, s>>>(a);
-  else merge_kernel<64><<<grid, dim3(kThreads), 0, s>>>(a);
+  const bool i32 = (int64_t)a.B * a.L * a.H < ((int64_t)1 << 31);
+  if (a.d == 128) {
+    if (i32) merge_kernel<128, true><<<grid, dim3(kThreads), 0, s>>>(a);
+    else merge_kernel<128, false><<<grid, dim3(kThreads), 0, s>>>(a);
+  } else {
+    if (i32) merge_kernel<64, true><<<grid, dim3(kThreads), 0, s>>>(a);
+    else merge_kernel<64, false><<<grid, dim3(kThreads), 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

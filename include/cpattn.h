@@ -108,8 +108,10 @@ typedef struct {
   float* l;
 } cp_state;
 
-/* Opaque per-launch timer (HIP events recorded around each attention kernel
- * of cp_attn_rank_forward on the compute stream). */
+/* Opaque per-launch timer: HIP events recorded around each attention kernel
+ * of cp_attn_rank_forward (and _fp8, _static) on the compute stream, and
+ * around each ring receive on the stream that carries it (the copy stream
+ * with CP_RING_PREFETCH, else the compute stream). */
 typedef struct cp_attn_profiler cp_attn_profiler;
 
 /* One block of the online-softmax recurrence (compassingai.com page, section
@@ -347,14 +349,31 @@ cp_status cp_attn_ring_schedule(const cp_attn_desc* desc, int32_t flags, int32_t
  * flops).  Errors: CP_ERR_INVALID_ARG. */
 cp_status cp_attn_visible_pairs(const cp_attn_desc* desc, int64_t* pairs_out);
 
-/* Profiler: capacity = number of kernel launches it can time; records
- * beyond capacity are dropped.  read() waits for the recorded events and
- * writes each launch's duration in milliseconds; reset() forgets them. */
+/* Profiler: capacity = number of kernel launches (and, separately, of ring
+ * receives) it can time; records beyond capacity are dropped.  read() waits
+ * for the recorded events and writes each attention launch's duration in
+ * milliseconds; read_copies() does the same for each ring receive (the
+ * device-to-device copy of K_j and the re-layout of V_j into a workspace
+ * slot: the simulated communication of one ring step, compassingai.com page,
+ * section "關鍵指標", communication/computation ratio); reset() forgets both.
+ * Errors: CP_ERR_INVALID_ARG (capacity too small, NULL arguments),
+ * CP_ERR_HIP. */
 cp_status cp_attn_profiler_create(int32_t capacity, cp_attn_profiler** out);
 cp_status cp_attn_profiler_reset(cp_attn_profiler* prof);
 cp_status cp_attn_profiler_read(cp_attn_profiler* prof, float* ms_out, int32_t capacity,
                                 int32_t* count_out);
+cp_status cp_attn_profiler_read_copies(cp_attn_profiler* prof, float* ms_out, int32_t capacity,
+                                       int32_t* count_out);
 void cp_attn_profiler_destroy(cp_attn_profiler* prof);
+
+/* Measurement helper (not part of the method): read `bytes` of device memory
+ * at src once through the global -> LDS fetch the attention kernels use for
+ * their K/V tiles (16 bytes per lane), discarding the data.  A profiler's
+ * count of HBM bytes fetched for this kernel against `bytes` calibrates the
+ * same counter read for the attention kernels.  src: device, 16-byte
+ * aligned; bytes: a positive multiple of 4096.  Asynchronous on `stream`.
+ * Errors: CP_ERR_INVALID_ARG, CP_ERR_HIP. */
+cp_status cp_attn_measure_lds_stream(const void* src, size_t bytes, void* stream);
 
 /* Static name of a status code. */
 const char* cp_attn_status_string(int32_t status);

@@ -268,6 +268,14 @@ def test_rank_forward_static_argument_errors():
         assert msg in B.last_error(), (msg, B.last_error())
 
 
+def test_measure_lds_stream_argument_errors():
+    lib = B.lib()
+    for args, msg in (((None, 4096, None), "src is NULL"), ((FAKE + 8, 4096, None), "16-byte"),
+                      ((FAKE, 0, None), "multiple of 4096"), ((FAKE, 4097, None), "multiple of 4096")):
+        assert _status(lib.cp_attn_measure_lds_stream, *args) == B.CP_ERR_INVALID_ARG
+        assert msg in B.last_error(), (msg, B.last_error())
+
+
 def test_host_query_argument_errors():
     lib = B.lib()
     d = _desc()

@@ -185,6 +185,31 @@ def test_prefetch_and_direction(cp):
     _check_all(c, ref, "bf16")
 
 
+@pytest.mark.parametrize("flags", ["forward", "reverse"])
+def test_document_rows_per_step(cp, flags):
+    """Under the document mask each step runs only the shard rows that see
+    its block (a prefix of the shard), and a row stores its final output at
+    the last step that sees it.  Documents spanning several blocks make the
+    prefixes differ per block; in the reverse ring order they grow from step
+    to step instead of shrinking.  Every rank of a 5-block ring of ragged
+    shards (L = 200, rows in several query tiles), against the oracle, with
+    the ring prefetch on and off bit-identical."""
+    N, L, H, d = 5, 200, 2, 128
+    cu = np.asarray([0, 150, 330, 333, 620, 1000], np.int32)   # documents across 1, 2 and 3 blocks
+    spec = ShardSpec(S=N * L, N=N, H=H, d=d, dtype="bf16", mask="doc_causal", cfg_id=110, cu_seqlens=cu)
+    inp = make_inputs(spec, seed=11, ranks=range(N))
+    kb, vb = _blocks(spec, inp)
+    fl = cp.CP_RING_REVERSE if flags == "reverse" else 0
+    for r in range(N):
+        say(f"[document rows] {flags} rank {r}")
+        got = run_rank(cp, spec, r, dev(inp["q"][r], "bf16"), kb, vb, fl | cp.CP_RING_PREFETCH)
+        serial = run_rank(cp, spec, r, dev(inp["q"][r], "bf16"), kb, vb, fl)
+        for x, y in zip(got, serial):
+            assert np.array_equal(x, y)
+        ref = oracle.rank_attention(inp["q"][r], inp["k"], inp["v"], r, N, "doc_causal", cu)
+        _check_all(got, ref, "bf16")
+
+
 @pytest.mark.parametrize("mask", ["causal", "doc_causal"])
 def test_invisible_blocks_are_never_read(cp, mask):
     """Blocks the schedule skips are filled with NaN: outputs stay finite and
@@ -437,7 +462,7 @@ def test_invisible_block_through_block_partial(cp, dtype):
     assert torch.all(st[0] == 0) and torch.all(torch.isneginf(st[1])) and torch.all(st[2] == 0)
 
 
-def test_profiler_records_each_attention_launch(cp):
+def test_profiler_records_each_launch_and_receive(cp):
     spec = ShardSpec(S=4 * 384, N=4, H=2, d=128, dtype="bf16", mask="causal", cfg_id=109)
     inp = make_inputs(spec, seed=10, ranks=[2])
     kb, vb = _blocks(spec, inp)
@@ -453,8 +478,10 @@ def test_profiler_records_each_attention_launch(cp):
     cs.synchronize()
     times = prof.read()
     assert len(times) == 6 and all(t > 0 for t in times)      # rank 2 visits blocks 2, 1, 0 per call
+    copies = prof.read_copies()
+    assert len(copies) == 4 and all(t > 0 for t in copies)    # blocks 1 and 0 are received per call
     prof.reset()
-    assert prof.read() == []
+    assert prof.read() == [] and prof.read_copies() == []
     prof.close()
 
 
