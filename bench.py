@@ -50,13 +50,25 @@ KERNELS = {
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", KERNELS["bf16"]["json"])
 
 
+def kernel_device_text(path: str) -> bytes:
+    """The part of a kernel source that is device code: a .hip file up to its
+    first host launcher (`hipError_t launch_`), a header whole.  Launcher
+    changes that leave the kernel, its grid and its arguments as they were do
+    not invalidate a traffic measurement."""
+    with open(path, "rb") as f:
+        text = f.read()
+    if path.endswith(".hip"):
+        cut = text.find(b"\nhipError_t launch_")
+        if cut >= 0:
+            text = text[:cut]
+    return text
+
+
 def kernel_sha256(which: str = "bf16") -> str:
-    """SHA-256 over the sources a forward block kernel is compiled from."""
+    """SHA-256 over the device code a forward block kernel is compiled from."""
     h = hashlib.sha256()
     for f in KERNELS[which]["srcs"]:
-        path = os.path.join(ROOT, "context_ring_attention_cp_amd", "csrc", f)
-        with open(path, "rb") as f:
-            h.update(f.read())
+        h.update(kernel_device_text(os.path.join(ROOT, "context_ring_attention_cp_amd", "csrc", f)))
     return h.hexdigest()
 
 

@@ -23,7 +23,7 @@ CP_F32, CP_BF16 = 0, 1
 CP_MODE_INIT, CP_MODE_ACCUMULATE, CP_MODE_PARTIAL_LSE = 0, 1, 2
 CP_RING_PREFETCH, CP_RING_REVERSE = 1, 2
 CP_MAX_RING = 64
-CP_STATIC_SCRATCH_BYTES = 64 << 20
+CP_STATIC_SCRATCH_BYTES = 96 << 20
 
 MASKS = {"none": CP_MASK_NONE, "causal": CP_MASK_CAUSAL, "doc_causal": CP_MASK_DOC_CAUSAL}
 DTYPES = {"f32": CP_F32, "bf16": CP_BF16}

@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -42,9 +43,80 @@ COMMON = [
 ]
 
 
-def _compile(src: str) -> str:
+# Placement of the bf16 block kernel's main loop (attn_mfma.hip): each form's
+# loop should start at this byte offset within a 32-byte instruction block
+# (16-28 run fastest on the full-block form; 20 measured best there, 24 on the
+# diagonal form).  The build reads where the loop lands and pads the kernel
+# entry with no-ops (CP_LOOP_PAD_<D>_<VT>) until it starts there.
+LOOP_FORMS = {(128, 1): 20, (128, 0): 24, (64, 1): 20, (64, 0): 20}
+LLVM = os.environ.get("ROCM_LLVM", "/opt/rocm/llvm/bin")
+
+
+def _pad_defs(pads: dict) -> list:
+    return [f"-DCP_LOOP_PAD_{d}_{vt}={k}" for (d, vt), k in pads.items()]
+
+
+def _loop_offsets(pads: dict) -> dict:
+    """Byte offset of each form's main loop (the backward branch spanning the
+    most MFMAs) from its kernel's entry, for the given no-op pads."""
+    src = "attn_mfma.hip"
+    asm = os.path.join(BUILD, "placement.s")
+    obj = os.path.join(BUILD, "placement.o")
+    cmd = ([HIPCC] + COMMON + EXTRA.get(src, []) + _pad_defs(pads) +
+           ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm])
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr[-3000:]}")
+    subprocess.run([os.path.join(LLVM, "llvm-mc"), "-triple=amdgcn-amd-amdhsa", f"-mcpu={ARCH}", "-filetype=obj",
+                    asm, "-o", obj], check=True, capture_output=True)
+    dis = subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", "--no-show-raw-insn", obj],
+                         capture_output=True, text=True, check=True).stdout
+    out = {}
+    for sec in dis.split("Disassembly of section")[1:]:
+        m = re.search(r"attn_block_bf16_kernelILi(\d+)ELb(\d)E", sec.split("\n")[0])
+        if not m:
+            continue
+        insns = []   # (address, text)
+        for line in sec.split("\n"):
+            a = re.search(r"// ([0-9A-F]+):", line)
+            if a:
+                insns.append((int(a.group(1), 16), line))
+        best, best_n = None, 0
+        for addr, line in insns:
+            b = re.search(r"s_branch \d+.*<.*\+0x([0-9a-f]+)>", line)
+            if b and int(b.group(1), 16) < addr:
+                tgt = int(b.group(1), 16)
+                n = sum(1 for a2, l2 in insns if tgt <= a2 < addr and "v_mfma" in l2)
+                if n > best_n:
+                    best, best_n = tgt, n
+        if best is not None:
+            out[(int(m.group(1)), int(m.group(2)))] = best
+    return out
+
+
+def _placement_pads(verbose: bool) -> dict:
+    pads = {f: 0 for f in LOOP_FORMS}
+    for _ in range(6):
+        offs = _loop_offsets(pads)
+        off = {f: offs[f] % 32 for f in LOOP_FORMS}
+        if all(off[f] == LOOP_FORMS[f] for f in LOOP_FORMS):
+            break
+        for f in LOOP_FORMS:
+            if off[f] != LOOP_FORMS[f]:
+                pads[f] = (pads[f] + ((LOOP_FORMS[f] - off[f]) % 32) // 4) % 8
+    else:
+        bad = {f: o for f, o in off.items() if not 16 <= o <= 28}
+        if bad:
+            print(f"warning: main loop placement off target: {bad}", file=sys.stderr)
+    if verbose:
+        print("main loop offsets mod 32: " + ", ".join(f"<{d},{bool(vt)}> {off[(d, vt)]} (pad {pads[(d, vt)]})"
+                                                        for d, vt in LOOP_FORMS))
+    return pads
+
+
+def _compile(src: str, defs: list = ()) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + list(defs) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in line)
@@ -58,7 +130,11 @@ def _compile(src: str) -> str:
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        # the other sources compile while the bf16 kernel's loop placement is found
+        rest = {src: ex.submit(_compile, src) for src in SOURCES if src != "attn_mfma.hip"}
+        pads = _placement_pads(verbose)
+        objs = [_compile("attn_mfma.hip", _pad_defs(pads)) if src == "attn_mfma.hip" else rest[src].result()
+                for src in SOURCES]
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -137,6 +138,44 @@ int64_t rows_seeing(const cp_attn_desc* d, int32_t j) {
   return r < 0 ? 0 : (r > d->L ? d->L : r);
 }
 
+// Dispatch order of the bf16 kernel's query tiles for block j under the
+// document mask: the tiles of the launch's rows by decreasing number of key
+// tiles they run (the key range a workgroup covers, from the document start
+// of its first row to the causal end of its last), so that the longest
+// workgroups start first.  Other masks keep the kernel's own order (the
+// causal work falls with the tile index already).
+void fill_order(const cp_attn_desc* d, int32_t j, BlockArgs& a) {
+  a.order_n = 0;
+  if (d->mask != CP_MASK_DOC_CAUSAL) return;
+  const int64_t nqt = (a.rows_end + kBf16Rows - 1) / kBf16Rows;
+  if (nqt < 2 || nqt > kOrderMax) return;
+  const int64_t L = d->L, nkt = (L + kBf16Keys - 1) / kBf16Keys;
+  const int64_t q_pos0 = (int64_t)d->rank * L, k_pos0 = (int64_t)j * L;
+  auto doc_start = [&](int64_t p) {   // start of the document holding global position p
+    int lo = 0, hi = d->ndocs;
+    while (lo < hi) {
+      const int mid = (lo + hi) / 2;
+      if ((int64_t)d->cu_seqlens[mid + 1] > p) hi = mid; else lo = mid + 1;
+    }
+    return (int64_t)d->cu_seqlens[lo < d->ndocs ? lo : d->ndocs - 1];
+  };
+  std::vector<std::pair<int64_t, int32_t>> w((size_t)nqt);
+  for (int64_t qt = 0; qt < nqt; ++qt) {
+    const int64_t q0 = qt * kBf16Rows, q_last = std::min(q0 + kBf16Rows, a.rows_end) - 1;
+    const int64_t hi = q_pos0 + q_last - k_pos0;
+    const int64_t kt_end = hi < 0 ? 0 : std::min(hi / kBf16Keys + 1, nkt);
+    const int64_t lo = doc_start(q_pos0 + q0) - k_pos0;
+    const int64_t kt_begin = lo > 0 ? std::min(lo / kBf16Keys, nkt) : 0;
+    w[(size_t)qt] = {std::max<int64_t>(kt_end - kt_begin, 0), (int32_t)qt};
+  }
+  // decreasing work; among equals the higher tile first (the kernel's own order)
+  std::sort(w.begin(), w.end(), [](const auto& x, const auto& y) {
+    return x.first != y.first ? x.first > y.first : x.second > y.second;
+  });
+  for (int64_t r = 0; r < nqt; ++r) a.order[r] = (uint16_t)w[(size_t)r].second;
+  a.order_n = (int32_t)nqt;
+}
+
 std::vector<int32_t> schedule(const cp_attn_desc* d, int32_t flags) {
   std::vector<int32_t> out;
   const int step = (flags & CP_RING_REVERSE) ? 1 : -1;
@@ -172,16 +211,38 @@ BlockArgs block_args(const cp_attn_desc* d, int32_t j, const void* q, const void
   return a;
 }
 
-hipError_t launch_block(const cp_attn_desc* d, const BlockArgs& a, hipStream_t s) {
-  return d->dtype == CP_BF16 ? launch_block_bf16(a, d->d, s) : launch_block_f32(a, d->d, s);
+hipError_t launch_block(const cp_attn_desc* d, const BlockArgs& a, hipStream_t s, const LaunchEvents& ev = {}) {
+  return d->dtype == CP_BF16 ? launch_block_bf16(a, d->d, s, ev) : launch_block_f32(a, d->d, s, ev);
 }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Key split of the causal diagonal block (the first ring step) when its launch
+// would fill the chip's 256 compute units at most once: the heaviest query
+// tiles then set the launch's length alone, and splitting the keys of the upper
+// half of the tiles between two workgroups halves it.  The next step (a full
+// block, seen by every row) merges the two states.  bf16 only.
+constexpr int64_t kSplitMaxWorkgroups = 256;
+
+bool split_eligible(const cp_attn_desc* d) {
+  const int64_t nqt = (d->L + kBf16Rows - 1) / kBf16Rows;
+  return d->dtype == CP_BF16 && d->mask == CP_MASK_CAUSAL && d->rank >= 1 && nqt >= 2 &&
+         nqt * d->H * d->B <= kSplitMaxWorkgroups;
+}
+
+// First split query tile: the upper half of the tiles.
+int32_t split_from_of(const cp_attn_desc* d) {
+  const int64_t nqt = (d->L + kBf16Rows - 1) / kBf16Rows;
+  return (int32_t)(nqt - nqt / 2);
+}
+
 struct WorkspaceLayout {
-  size_t slot_k[2], slot_v[2], st_o, st_m, st_l, total;
+  size_t slot_k[2], slot_v[2], st_o, st_m, st_l, side_o, side_m, side_l, total;
+  bool side;
 };
 
+// With room for the side state of a key-split diagonal block where
+// split_eligible holds.
 WorkspaceLayout layout_of(const cp_attn_desc* d) {
   WorkspaceLayout w;
   const size_t blk = round_up((size_t)d->B * d->L * d->H * d->d * elt_bytes(d->dtype), 256);
@@ -202,6 +263,16 @@ WorkspaceLayout layout_of(const cp_attn_desc* d) {
   off += vec;
   w.st_l = off;
   off += vec;
+  w.side = split_eligible(d);
+  w.side_o = w.side_m = w.side_l = 0;
+  if (w.side) {
+    w.side_o = off;
+    off += ost;
+    w.side_m = off;
+    off += vec;
+    w.side_l = off;
+    off += vec;
+  }
   w.total = off;
   return w;
 }
@@ -587,8 +658,13 @@ static cp_status rank_forward_impl(const cp_attn_desc* desc, const void* q, cons
   // contiguous run and reads V^T operands as whole 16-byte rows)
   const bool v_tiled = fp8 || desc->dtype == CP_BF16;
 
-  // ready[t]: block of step t is in its slot; done[t]: step t's kernel finished with its slot
+  // ready[t]: block of step t is in its slot; done[t]: step t's kernel
+  // finished with its slot.  Both are bound to the dispatch they follow (the
+  // receive's last kernel, the attention kernel), so that the cross-stream
+  // dependencies add no marker packets between dependent kernels; with a
+  // profiler its events take those places.
   std::vector<hipEvent_t> ready(nsteps, nullptr), done(nsteps, nullptr);
+  std::vector<hipEvent_t> ready_at(nsteps, nullptr), done_at(nsteps, nullptr);   // the events to wait for
   hipError_t e = hipSuccess;
   hipEvent_t start_ev = nullptr;   // the copy stream's start (inputs ready), with prefetch
   auto cleanup = [&]() {
@@ -598,15 +674,16 @@ static cp_status rank_forward_impl(const cp_attn_desc* desc, const void* q, cons
   };
   if (prefetch) {
     for (int32_t t = 0; t < nsteps; ++t) {
-      if ((e = hipEventCreateWithFlags(&ready[t], hipEventDisableTiming)) != hipSuccess ||
-          (e = hipEventCreateWithFlags(&done[t], hipEventDisableTiming)) != hipSuccess) {
+      if ((e = hipEventCreate(&ready[t])) != hipSuccess || (e = hipEventCreate(&done[t])) != hipSuccess) {
         cleanup();
-        return hip_fail(e, "hipEventCreateWithFlags");
+        return hip_fail(e, "hipEventCreate");
       }
     }
   }
   auto slot_k = [&](int32_t t) { return (void*)(ws + wl.slot_k[t & 1]); };
   auto slot_v = [&](int32_t t) { return (void*)(ws + wl.slot_v[t & 1]); };
+  // The receive of step t into its slots; with prefetch, ready_at[t] is set to
+  // the event that completes with it.
   auto enqueue_copy = [&](int32_t t, hipStream_t s) -> hipError_t {
     const int32_t j = sched[t];
     const bool timed = prof && prof->copies < (int32_t)prof->copy_start.size();
@@ -614,14 +691,18 @@ static cp_status rank_forward_impl(const cp_attn_desc* desc, const void* q, cons
     if (timed && (r = hipEventRecord(prof->copy_start[prof->copies], s)) != hipSuccess) return r;
     r = hipMemcpyAsync(slot_k(t), k_blocks[j], blk_bytes, hipMemcpyDeviceToDevice, s);
     if (r != hipSuccess) return r;
-    if (v_tiled && fp8) r = launch_v_tiles_fp8(v_blocks[j], slot_v(t), desc->L, desc->B, desc->H, desc->d, s);
-    else if (v_tiled) r = launch_v_tiles(v_blocks[j], slot_v(t), desc->L, desc->B, desc->H, desc->d, s);
-    else r = hipMemcpyAsync(slot_v(t), v_blocks[j], blk_bytes, hipMemcpyDeviceToDevice, s);
-    if (r != hipSuccess) return r;
-    if (timed) {
-      if ((r = hipEventRecord(prof->copy_stop[prof->copies], s)) != hipSuccess) return r;
-      prof->copies++;
+    hipEvent_t fin = timed ? prof->copy_stop[prof->copies] : (prefetch ? ready[t] : nullptr);
+    if (v_tiled) {
+      const LaunchEvents ev{nullptr, fin};
+      r = fp8 ? launch_v_tiles_fp8(v_blocks[j], slot_v(t), desc->L, desc->B, desc->H, desc->d, s, ev)
+              : launch_v_tiles(v_blocks[j], slot_v(t), desc->L, desc->B, desc->H, desc->d, s, ev);
+    } else {
+      r = hipMemcpyAsync(slot_v(t), v_blocks[j], blk_bytes, hipMemcpyDeviceToDevice, s);
+      if (r == hipSuccess && fin) r = hipEventRecord(fin, s);
     }
+    if (r != hipSuccess) return r;
+    if (timed) prof->copies++;
+    if (prefetch) ready_at[t] = fin;
     return hipSuccess;
   };
   // The copy stream starts after everything already queued on the compute
@@ -641,8 +722,7 @@ static cp_status rank_forward_impl(const cp_attn_desc* desc, const void* q, cons
     (void)hipEventDestroy(start_ev);
     start_ev = nullptr;
     if (r != hipSuccess) return r;
-    if ((r = enqueue_copy(1, xs)) != hipSuccess) return r;
-    return hipEventRecord(ready[1], xs);
+    return enqueue_copy(1, xs);
   };
 
   for (int32_t t = 0; t < nsteps; ++t) {
@@ -650,7 +730,7 @@ static cp_status rank_forward_impl(const cp_attn_desc* desc, const void* q, cons
     const void* kp = t == 0 ? k_blocks[j] : slot_k(t);
     const void* vp = t == 0 ? v_blocks[j] : slot_v(t);
     if (t > 0) {
-      if (prefetch) e = hipStreamWaitEvent(cs, ready[t], 0);
+      if (prefetch) e = hipStreamWaitEvent(cs, ready_at[t], 0);
       else e = enqueue_copy(t, cs);
       if (e != hipSuccess) { cleanup(); return hip_fail(e, "ring receive"); }
     }
@@ -674,23 +754,33 @@ static cp_status rank_forward_impl(const cp_attn_desc* desc, const void* q, cons
     a.st_o = (float*)(ws + wl.st_o);
     a.st_m = (float*)(ws + wl.st_m);
     a.st_l = (float*)(ws + wl.st_l);
+    if (!fp8) fill_order(desc, j, a);
+    if (wl.side && !fp8 && t < 2) {
+      // key split of the diagonal block (step 0, the rank's own block), merged
+      // by step 1 (a full block: every row reads its state there)
+      a.flags |= t == 0 ? F_SPLIT : F_READ_SIDE;
+      a.split_from = split_from_of(desc);
+      a.side_o = (float*)(ws + wl.side_o);
+      a.side_m = (float*)(ws + wl.side_m);
+      a.side_l = (float*)(ws + wl.side_l);
+    }
     a.out = out;
     a.m_out = m_out;
     a.l_out = l_out;
     a.lse_out = lse_out;
+    // the receive for step t+2 reuses the slot of step t: it waits for this kernel
+    const bool reuse = prefetch && t + 1 < nsteps - 1;
     const bool timed = prof && prof->used < (int32_t)prof->start.size();
-    if (timed && (e = hipEventRecord(prof->start[prof->used], cs)) != hipSuccess) { cleanup(); return hip_fail(e, "profiler record"); }
-    e = fp8 ? launch_block_fp8(a, desc->d, cs) : launch_block(desc, a, cs);
+    LaunchEvents ev;
+    if (timed) ev = LaunchEvents{prof->start[prof->used], prof->stop[prof->used]};
+    else if (reuse) ev.stop = done[t];
+    e = fp8 ? launch_block_fp8(a, desc->d, cs, ev) : launch_block(desc, a, cs, ev);
     if (e != hipSuccess) { cleanup(); return hip_fail(e, "block kernel launch"); }
-    if (timed) {
-      if ((e = hipEventRecord(prof->stop[prof->used], cs)) != hipSuccess) { cleanup(); return hip_fail(e, "profiler record"); }
-      prof->used++;
-    }
+    if (timed) prof->used++;
+    done_at[t] = ev.stop;
     if (t == 0 && start_ev && (e = start_copies()) != hipSuccess) { cleanup(); return hip_fail(e, "ring receive copy"); }
-    if (prefetch && t + 1 < nsteps - 1) {
-      // the receive for step t+2 reuses the slot of step t: wait for this kernel
-      if ((e = hipEventRecord(done[t], cs)) != hipSuccess || (e = hipStreamWaitEvent(xs, done[t], 0)) != hipSuccess ||
-          (e = enqueue_copy(t + 2, xs)) != hipSuccess || (e = hipEventRecord(ready[t + 2], xs)) != hipSuccess) {
+    if (reuse) {
+      if ((e = hipStreamWaitEvent(xs, done_at[t], 0)) != hipSuccess || (e = enqueue_copy(t + 2, xs)) != hipSuccess) {
         cleanup();
         return hip_fail(e, "ring receive copy");
       }

@@ -168,12 +168,12 @@ __global__ __launch_bounds__(kThreads) void attn_block_f32_kernel(BlockArgs a) {
 
 }  // namespace
 
-hipError_t launch_block_f32(const BlockArgs& a, int d, hipStream_t s) {
+hipError_t launch_block_f32(const BlockArgs& a, int d, hipStream_t s, const LaunchEvents& ev) {
+  if (a.flags & (F_SPLIT | F_READ_SIDE)) return hipErrorInvalidValue;   // bf16 kernel only
   const int64_t nqt = (a.rows_end + kRows - 1) / kRows;
-  const int64_t nwg = nqt * a.H * a.B;
-  if (d == 128) attn_block_f32_kernel<128><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
-  else attn_block_f32_kernel<64><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
-  return hipGetLastError();
+  const dim3 grid((unsigned)(nqt * a.H * a.B)), block(kThreads);
+  return d == 128 ? launch_bound(attn_block_f32_kernel<128>, grid, block, s, ev, a)
+                  : launch_bound(attn_block_f32_kernel<64>, grid, block, s, ev, a);
 }
 
 }  // namespace cpattn

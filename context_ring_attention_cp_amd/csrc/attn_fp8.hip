@@ -500,18 +500,16 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
 
 }  // namespace
 
-hipError_t launch_block_fp8(const BlockArgs& a, int d, hipStream_t s) {
+hipError_t launch_block_fp8(const BlockArgs& a, int d, hipStream_t s, const LaunchEvents& ev) {
+  if (a.flags & (F_SPLIT | F_READ_SIDE)) return hipErrorInvalidValue;   // bf16 kernel only
   const int64_t nqt = (a.rows_end + BM - 1) / BM;
-  const int64_t nwg = nqt * a.H * a.B;
+  const dim3 grid((unsigned)(nqt * a.H * a.B)), block(kThreads);
   const bool vt = (a.flags & F_V_TILED) != 0;
-  if (d == 128) {
-    if (vt) attn_block_fp8_kernel<128, true><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
-    else attn_block_fp8_kernel<128, false><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
-  } else {
-    if (vt) attn_block_fp8_kernel<64, true><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
-    else attn_block_fp8_kernel<64, false><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
-  }
-  return hipGetLastError();
+  if (d == 128)
+    return vt ? launch_bound(attn_block_fp8_kernel<128, true>, grid, block, s, ev, a)
+              : launch_bound(attn_block_fp8_kernel<128, false>, grid, block, s, ev, a);
+  return vt ? launch_bound(attn_block_fp8_kernel<64, true>, grid, block, s, ev, a)
+            : launch_bound(attn_block_fp8_kernel<64, false>, grid, block, s, ev, a);
 }
 
 }  // namespace cpattn

@@ -67,11 +67,42 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int BM = 32 * kWaves;   // query rows per workgroup
 constexpr int BN = 64;            // keys per LDS tile
+static_assert(BM == kBf16Rows && BN == kBf16Keys, "host tile constants");
 constexpr int kStages = 4;        // LDS ring depth
 constexpr float kLazy = 8.0f;     // log2 headroom before a rescale
 
+// Code placement.  The main loop runs up to 3.5 % slower when it starts in the
+// first half of a 32-byte instruction block (offsets 0-12 mod 32 against
+// 16-28, measured on the full-block form).  The build counts where each form's
+// main loop lands and sets CP_LOOP_PAD_<D>_<VT>: that many 4-byte no-ops at the
+// kernel entry (run once per wave) move the loop to the offset it aims for.
+#ifndef CP_LOOP_PAD_128_1
+#define CP_LOOP_PAD_128_1 0
+#endif
+#ifndef CP_LOOP_PAD_128_0
+#define CP_LOOP_PAD_128_0 0
+#endif
+#ifndef CP_LOOP_PAD_64_1
+#define CP_LOOP_PAD_64_1 0
+#endif
+#ifndef CP_LOOP_PAD_64_0
+#define CP_LOOP_PAD_64_0 0
+#endif
+#define CP_STR2(x) #x
+#define CP_STR(x) CP_STR2(x)
+#define CP_NOPS(n) asm volatile(".rept " CP_STR(n) "\n s_nop 0\n .endr")
+
+template <int D, bool VT>
+__device__ __forceinline__ void loop_placement() {
+  if constexpr (D == 128 && VT) CP_NOPS(CP_LOOP_PAD_128_1);
+  else if constexpr (D == 128) CP_NOPS(CP_LOOP_PAD_128_0);
+  else if constexpr (VT) CP_NOPS(CP_LOOP_PAD_64_1);
+  else CP_NOPS(CP_LOOP_PAD_64_0);
+}
+
 template <int D, bool VT>
 __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) {
+  loop_placement<D, VT>();
   constexpr int CH = D / 8;          // 16-byte chunks per row
   constexpr int NS = D / 16;         // k-steps of S^T = K Q^T
   constexpr int NDT = D / 32;        // 32-row tiles of O^T
@@ -91,17 +122,53 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   const int64_t L = a.L;
   const int H = a.H;
 
-  // Workgroup -> (batch, head, query tile).  Workgroups are dispatched to the
+  // Workgroup -> (batch, head, work item).  Workgroups are dispatched to the
   // 8 XCDs round robin; the remap gives each XCD a contiguous run of logical
   // ids (one head's query tiles share its K/V in that XCD's L2).  Within a
-  // head, the query tiles that see the most keys start first.
+  // head, the items with the most keys start first.  An item is a query tile,
+  // or with F_SPLIT one of the two key ranges of a split tile: the nsp tiles
+  // from nlo on are split, first the nsp lower key ranges (nlo tiles' worth of
+  // keys each), then the unsplit tiles above the pairs, then for m = nsp .. 1
+  // the upper key range of tile nlo + m - 1 and the unsplit tile m - 1 (m
+  // tiles' worth of keys each, for a causal diagonal block).  With a host-given
+  // order (document masks), the tiles of an XCD's heads run rank by rank
+  // instead: the heaviest tile of each head first.
   const int64_t rows_end = a.rows_end;                     // rows taking part in this launch
   const int nqt = (int)((rows_end + BM - 1) / BM);
-  const int64_t nwg = (int64_t)nqt * H * a.B;
+  const bool split = a.flags & F_SPLIT;
+  const int nlo = split ? a.split_from : nqt;              // tiles below the split ones
+  const int nsp = nqt - nlo;
+  const int items = nqt + nsp;
+  const int64_t nwg = (int64_t)items * H * a.B;
   const int64_t bid = blockIdx.x;
   const int64_t logical = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
-  const int64_t hb = logical / nqt;
-  const int qt = nqt - 1 - (int)(logical % nqt);
+  int64_t hb = logical / items;
+  const int it = (int)(logical % items);
+  int qt = nqt - 1 - it;
+  int part = 0;                                            // 1: lower key range of a split tile, 2: upper
+  if (!split && a.order_n == nqt) {
+    // host-given order by decreasing work; rank-major over the whole heads of an XCD
+    const int64_t per = nwg / 8;
+    if (nwg % 8 == 0 && per % nqt == 0) {
+      const int64_t hpx = per / nqt, j = logical % per;
+      hb = (logical / per) * hpx + j % hpx;
+      qt = a.order[j / hpx];
+    } else {
+      qt = a.order[it];
+    }
+  }
+  if (split) {
+    const int extra = nlo - nsp;
+    if (it < nsp) {
+      part = 1;
+    } else if (it - nsp < extra) {
+      qt = nlo - 1 - (it - nsp);
+    } else {
+      const int pp = it - nsp - extra, m = nsp - pp / 2;
+      qt = (pp & 1) ? m - 1 : nlo + m - 1;
+      part = (pp & 1) ? 0 : 2;
+    }
+  }
   const int h = (int)(hb % H);
   const int b = (int)(hb / H);
 
@@ -132,6 +199,9 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
         if (lo > 0) kt_begin = (int)(lo / BN < nkt ? lo / BN : nkt);
       }
     }
+    const int split_kt = nlo * (BM / BN);
+    if (part == 1 && kt_end > split_kt) kt_end = split_kt;
+    if (part == 2 && kt_begin < split_kt) kt_begin = split_kt;
   }
   const bool rd = a.flags & F_READ_STATE;
   // nothing to compute and nothing to store: the state of these rows stays as it is
@@ -462,20 +532,41 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   }
 
   if (!row_ok || qrow >= rows_end) return;
+  if ((a.flags & F_READ_SIDE) && qt >= a.split_from) {
+    // the other key range of a split tile: merge the two states at their common max
+    const float m2 = a.side_m[ml_idx] * kLog2e;
+    const float mt = fmaxf(m_true, m2);
+    const float c1 = m_true == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_true - mt);
+    const float c2s = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mt);
+    l_run = g == 0 ? c1 * l_run + c2s * a.side_l[ml_idx] : c1 * l_run;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 v4 = *(const float4*)(a.side_o + st_row + 32 * dt + 8 * i4 + 4 * g);
+        oacc[dt][4 * i4 + 0] = c1 * oacc[dt][4 * i4 + 0] + c2s * v4.x;
+        oacc[dt][4 * i4 + 1] = c1 * oacc[dt][4 * i4 + 1] + c2s * v4.y;
+        oacc[dt][4 * i4 + 2] = c1 * oacc[dt][4 * i4 + 2] + c2s * v4.z;
+        oacc[dt][4 * i4 + 3] = c1 * oacc[dt][4 * i4 + 3] + c2s * v4.w;
+      }
+    m_true = mt;
+  }
   const float l_tot = l_run + xor32(l_run);
   const bool has = l_tot > 0.f;
   const float m_run = m_true;
 
   if (writes_state(a.flags, qrow, a.final_from)) {
+    // the lower key range of a split tile keeps its state on the side
+    float* const so = part == 1 ? a.side_o : a.st_o;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4)
-        *(float4*)(a.st_o + st_row + 32 * dt + 8 * i4 + 4 * g) =
+        *(float4*)(so + st_row + 32 * dt + 8 * i4 + 4 * g) =
             float4{oacc[dt][4 * i4], oacc[dt][4 * i4 + 1], oacc[dt][4 * i4 + 2], oacc[dt][4 * i4 + 3]};
     if (g == 0) {
-      a.st_m[ml_idx] = m_run * kLn2;
-      a.st_l[ml_idx] = l_tot;
+      (part == 1 ? a.side_m : a.st_m)[ml_idx] = m_run * kLn2;
+      (part == 1 ? a.side_l : a.st_l)[ml_idx] = l_tot;
     }
   }
   const float inv = has ? 1.f / l_tot : 0.f;
@@ -511,18 +602,18 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
 
 }  // namespace
 
-hipError_t launch_block_bf16(const BlockArgs& a, int d, hipStream_t s) {
+hipError_t launch_block_bf16(const BlockArgs& a, int d, hipStream_t s, const LaunchEvents& ev) {
   const int64_t nqt = (a.rows_end + BM - 1) / BM;
-  const int64_t nwg = nqt * a.H * a.B;
+  // a key split covers the upper tiles of the launch, at most half of them
+  if ((a.flags & F_SPLIT) && (a.split_from >= nqt || 2 * (int64_t)a.split_from < nqt)) return hipErrorInvalidValue;
+  const int64_t items = (a.flags & F_SPLIT) ? 2 * nqt - a.split_from : nqt;
+  const dim3 grid((unsigned)(items * a.H * a.B)), block(kThreads);
   const bool vt = (a.flags & F_V_TILED) != 0;
-  if (d == 128) {
-    if (vt) attn_block_bf16_kernel<128, true><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
-    else attn_block_bf16_kernel<128, false><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
-  } else {
-    if (vt) attn_block_bf16_kernel<64, true><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
-    else attn_block_bf16_kernel<64, false><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(a);
-  }
-  return hipGetLastError();
+  if (d == 128)
+    return vt ? launch_bound(attn_block_bf16_kernel<128, true>, grid, block, s, ev, a)
+              : launch_bound(attn_block_bf16_kernel<128, false>, grid, block, s, ev, a);
+  return vt ? launch_bound(attn_block_bf16_kernel<64, true>, grid, block, s, ev, a)
+            : launch_bound(attn_block_bf16_kernel<64, false>, grid, block, s, ev, a);
 }
 
 }  // namespace cpattn

@@ -15,7 +15,15 @@ enum : int32_t {
   F_WRITE_PARTIAL = 8,  // store normalised O (float32) and lse of this block alone
   F_V_TILED = 16,       // v in head-dim-major key tiles, zero past L: bf16 [B, H, T, d, 64],
                         // e4m3 [B, H, T8, d, 128] with the operand key order (launch_v_tiles_fp8)
+  F_SPLIT = 32,         // bf16 kernel: split the keys of the query tiles from split_from on
+  F_READ_SIDE = 64,     // bf16 kernel: merge the side state of those tiles into the state read
 };
+
+// Query rows per workgroup of the bf16 block kernel, and keys per LDS tile.
+constexpr int kBf16Rows = 256;
+constexpr int kBf16Keys = 64;
+// Longest query-tile dispatch order a launch carries in its arguments.
+constexpr int kOrderMax = 512;
 
 // Per-row store decisions of a block launch (see BlockArgs::final_from).
 __host__ __device__ inline bool writes_final(int32_t flags, int64_t row, int64_t final_from) {
@@ -49,6 +57,19 @@ struct BlockArgs {
   // them the running state; with one of the two flags every row stores that.
   int64_t rows_end;
   int64_t final_from;
+  // Key split of a causal diagonal block (bf16 kernel).  With F_SPLIT, each
+  // query tile qt >= split_from (of kBf16Rows rows) runs as two workgroups:
+  // one takes the key tiles [0, split_from * kBf16Rows / kBf16Keys), which
+  // those rows all see, and stores its running state in side_*; the other
+  // takes the rest of the block and stores into st_*.  With F_READ_SIDE the
+  // rows of those tiles merge side_* into their state at the end of the launch
+  // (the merge of running states is associative: the launch may add its block
+  // to either part first).
+  // split_from >= (number of query tiles) / 2.
+  int32_t split_from;
+  float* side_o;         // [B, L, H, d]
+  float* side_m;         // [B, H, L] natural-log units
+  float* side_l;         // [B, H, L]
   // running state
   float* st_o;           // [B, L, H, d]
   float* st_m;           // [B, H, L] natural-log units
@@ -65,6 +86,13 @@ struct BlockArgs {
   const float* q_scale;  // [B, H] of the query shard
   const float* k_scale;  // [B, H] of block j
   const float* v_scale;  // [B, H] of block j
+  // Dispatch order of the query tiles (bf16 kernel, without F_SPLIT): when
+  // order_n equals the launch's number of query tiles, order[r] is the tile
+  // of rank r by decreasing work (the host computes it from the document
+  // boundaries), and an XCD that holds whole heads runs their tiles rank by
+  // rank; otherwise the tiles run in decreasing index.
+  int32_t order_n;
+  uint16_t order[kOrderMax];
 };
 
 // Largest merge count handled by one kernel launch.

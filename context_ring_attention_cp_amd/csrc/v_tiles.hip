@@ -113,20 +113,22 @@ __global__ __launch_bounds__(kThreadsT) void v_tiles_fp8_kernel(const uint8_t* _
 
 }  // namespace
 
-hipError_t launch_v_tiles(const void* v, void* v_tiled, int64_t L, int32_t B, int32_t H, int d, hipStream_t s) {
-  const int64_t nwg = v_tiled_keys(L) / kTile * H * B;
-  if (d == 128) v_tiles_kernel<128><<<dim3((unsigned)nwg), dim3(kThreadsT), 0, s>>>((const bf16*)v, (bf16*)v_tiled, L, H);
-  else v_tiles_kernel<64><<<dim3((unsigned)nwg), dim3(kThreadsT), 0, s>>>((const bf16*)v, (bf16*)v_tiled, L, H);
-  return hipGetLastError();
+hipError_t launch_v_tiles(const void* v, void* v_tiled, int64_t L, int32_t B, int32_t H, int d, hipStream_t s,
+                          const LaunchEvents& ev) {
+  const dim3 grid((unsigned)(v_tiled_keys(L) / kTile * H * B)), block(kThreadsT);
+  const bf16* src = (const bf16*)v;
+  bf16* dst = (bf16*)v_tiled;
+  return d == 128 ? launch_bound(v_tiles_kernel<128>, grid, block, s, ev, src, dst, L, H)
+                  : launch_bound(v_tiles_kernel<64>, grid, block, s, ev, src, dst, L, H);
 }
 
-hipError_t launch_v_tiles_fp8(const void* v, void* v_tiled, int64_t L, int32_t B, int32_t H, int d, hipStream_t s) {
-  const int64_t nwg = (L + 127) / 128 * H * B;
-  if (d == 128)
-    v_tiles_fp8_kernel<128><<<dim3((unsigned)nwg), dim3(kThreadsT), 0, s>>>((const uint8_t*)v, (uint8_t*)v_tiled, L, H);
-  else
-    v_tiles_fp8_kernel<64><<<dim3((unsigned)nwg), dim3(kThreadsT), 0, s>>>((const uint8_t*)v, (uint8_t*)v_tiled, L, H);
-  return hipGetLastError();
+hipError_t launch_v_tiles_fp8(const void* v, void* v_tiled, int64_t L, int32_t B, int32_t H, int d, hipStream_t s,
+                              const LaunchEvents& ev) {
+  const dim3 grid((unsigned)((L + 127) / 128 * H * B)), block(kThreadsT);
+  const uint8_t* src = (const uint8_t*)v;
+  uint8_t* dst = (uint8_t*)v_tiled;
+  return d == 128 ? launch_bound(v_tiles_fp8_kernel<128>, grid, block, s, ev, src, dst, L, H)
+                  : launch_bound(v_tiles_fp8_kernel<64>, grid, block, s, ev, src, dst, L, H);
 }
 
 }  // namespace cpattn

@@ -78,9 +78,9 @@ typedef enum {
 
 #define CP_MAX_RING 64      /* largest ring size N (and merge count n) accepted */
 
-/* Bytes of the static device scratch of cp_attn_rank_forward_static (64 MiB
+/* Bytes of the static device scratch of cp_attn_rank_forward_static (96 MiB
  * per GPU the library runs on, held until the process ends). */
-#define CP_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+#define CP_STATIC_SCRATCH_BYTES ((size_t)96 << 20)
 
 /* Problem description (the shard statement of the pages: Q_i, K_j, V_j of
  * shape (S/N) x H x d, rank i, ring size N, mask).  */

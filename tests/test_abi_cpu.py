@@ -104,6 +104,25 @@ def test_workspace_bytes():
     assert "rank" in B.last_error()
 
 
+def test_workspace_bytes_key_split():
+    """A causal bf16 shard with a step after its diagonal and at most 256
+    workgroups in the diagonal launch (query tiles of 256 rows x heads x
+    batch) also holds the side state of the diagonal's key split."""
+    L, H = 8192, 8
+    elems = L * H * 128
+    base = 4 * elems * 2 + elems * 4 + 2 * H * L * 4
+    side = elems * 4 + 2 * H * L * 4
+    got = B.cp_attn_workspace_bytes(_desc(N=4, L=L, rank=3, H=H))
+    assert base + side <= got <= base + side + 12 * 256
+    for kw in (dict(rank=0), dict(mask="none"), dict(mask="doc_causal", cu_seqlens=[0, 4 * L], cu_seqlens_dev=FAKE),
+               dict(H=2 * H), dict(dtype="f32")):
+        h = kw.pop("H", H)
+        d = _desc(N=4, L=L, rank=kw.pop("rank", 3), H=h, **kw)
+        eb = 4 if d.dtype == "f32" else 2
+        plain = 4 * elems * eb * h // H + elems * 4 * h // H + 2 * h * L * 4
+        assert plain <= B.cp_attn_workspace_bytes(d) <= plain + 8 * 256, kw
+
+
 BAD_DESCS = [
     (dict(B=0), B.CP_ERR_INVALID_ARG, "B="),
     (dict(H=0), B.CP_ERR_INVALID_ARG, "H="),

@@ -4,7 +4,7 @@ same inputs.  Both run the same kernels in the same order, so every output
 (out, m, l, lse) must be bit-identical.  Three calls in a row share the static
 scratch, each on a smaller shard than the one before and with the scratch
 holding the previous call's bytes: a 4096-token bf16 causal shard with ring
-prefetch (50 MiB of the 64 MiB scratch), a ragged document-masked bf16 shard
+prefetch (68 MB of the 96 MiB scratch, key-split side state included), a ragged document-masked bf16 shard
 at d = 64, and a tiny fp32 shard without prefetch.  A shard whose scratch
 would exceed the array is refused with CP_ERR_WORKSPACE before anything is
 enqueued.
