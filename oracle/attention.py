@@ -16,14 +16,14 @@ What it computes (all in float64):
   softmax(QK^T/sqrt(d_k))V formula); process-cxr.github.io page (sections
   "配置关注点" and "常见失败模式": document-boundary masks must hold across
   shards).
-* ``streaming_attention`` - the numerator/denominator streaming form of the
-  wangyu.me page (section "Attention 的流式计算"): accumulate sum_i s_i V_i and
-  sum_j s_j over K/V blocks, s = exp(q k^T / sqrt(d_k)), no max shift, divide
-  at the end.
-* ``online_merge`` - the blockwise online-softmax recurrence of the
-  compassingai.com page (section "線上 Softmax", the Ring Attention +
-  FlashAttention algorithm): running (O, m, l), per block m_ij, P_ij, l_ij,
-  rescale by exp(m - m_new), divide O by l at the end.
+* ``streaming_attention`` - the streaming form of the wangyu.me page (section
+  "Attention 的流式计算"): no max shift, the output is the ratio of the sum of
+  exp(score) V over the sum of exp(score); both sums are taken here over all
+  blocks' keys at once.
+* ``online_merge`` - the online-softmax form of the compassingai.com page
+  (section "線上 Softmax"): per-block partial states (O_j, m_j, l_j) folded
+  into a running state in the visiting order with the pairwise merge rule
+  (``_combine``), O / l at the end.
 * ``block_partial`` / ``merge_lse`` - per-block normalised partials (O_j, lse_j)
   and their log-sum-exp merge (the same recurrence written in lse form: the
   process-cxr.github.io page, section "Long Context Attention 中的通信", asks
@@ -217,21 +217,20 @@ def streaming_attention(q: np.ndarray, k_blocks: Sequence[np.ndarray],
                         v_blocks: Sequence[np.ndarray], p: np.ndarray,
                         c_blocks: Sequence[np.ndarray], mask: str, cu_seqlens=None,
                         scale: Optional[float] = None) -> np.ndarray:
-    """Numerator/denominator streaming form for rows q [R,d]: for each K/V
-    block add exp(score) * V to a numerator and exp(score) to a denominator,
-    with no max subtraction; return numerator / denominator.  Valid while
-    scores stay far below ~700 (float64 exp range)."""
+    """Rows q [R,d] against all K/V blocks in the streaming form of the
+    wangyu.me page (section "Attention 的流式计算"): no maximum is subtracted,
+    the output is a ratio of two sums over the visible keys, the weights
+    w = exp(score) times V over the weights alone.  Both sums run over every
+    block, so here they are taken over the blocks' keys concatenated.  Valid
+    while scores stay far below ~700 (float64 exp range)."""
     q = np.asarray(q, dtype=np.float64)
     d = q.shape[-1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    num = np.zeros_like(q)
-    den = np.zeros(q.shape[0])
-    for k, v, c in zip(k_blocks, v_blocks, c_blocks):
-        s = np.exp((q @ np.asarray(k, np.float64).T) * scale)
-        s = np.where(visibility(p, c, mask, cu_seqlens), s, 0.0)
-        den += s.sum(axis=1)
-        num += s @ np.asarray(v, np.float64)
-    return num / den[:, None]
+    k_all = np.concatenate([np.asarray(k, np.float64) for k in k_blocks])
+    v_all = np.concatenate([np.asarray(v, np.float64) for v in v_blocks])
+    c_all = np.concatenate([np.asarray(c) for c in c_blocks])
+    w = np.where(visibility(p, c_all, mask, cu_seqlens), np.exp((q @ k_all.T) * scale), 0.0)
+    return (w @ v_all) / w.sum(axis=1)[:, None]
 
 
 def _exp_shift(a: np.ndarray, b: np.ndarray) -> np.ndarray:
@@ -240,37 +239,45 @@ def _exp_shift(a: np.ndarray, b: np.ndarray) -> np.ndarray:
         return np.where(np.isneginf(a), 0.0, np.exp(a - np.where(np.isneginf(b), 0.0, b)))
 
 
+def _block_state(q: np.ndarray, k: np.ndarray, v: np.ndarray, p: np.ndarray, c: np.ndarray,
+                 mask: str, cu_seqlens, scale: float):
+    """The unnormalised partial state of rows q against one K/V block: m = the
+    row maximum of the visible scaled scores, l = the row sum of exp(score -
+    m), O = those exponentials times V.  A row that sees no key of the block
+    has m = -inf, l = 0, O = 0."""
+    S = np.where(visibility(p, c, mask, cu_seqlens), (q @ np.asarray(k, np.float64).T) * scale, -np.inf)
+    m = S.max(axis=1) if S.shape[1] else np.full(q.shape[0], -np.inf)
+    E = _exp_shift(S, m[:, None])
+    return E @ np.asarray(v, np.float64), m, E.sum(axis=1)
+
+
+def _combine(a, b):
+    """Merge two partial states (O, m, l) of the same rows: both are brought
+    to the larger of the two maxima and added (the merge step of the
+    compassingai.com page, section "線上 Softmax").  The rule is associative
+    and commutative up to rounding, which is what lets the blocks arrive in
+    any ring order."""
+    (oa, ma, la), (ob, mb, lb) = a, b
+    m = np.maximum(ma, mb)
+    wa, wb = _exp_shift(ma, m), _exp_shift(mb, m)
+    return oa * wa[:, None] + ob * wb[:, None], m, la * wa + lb * wb
+
+
 def online_merge(q: np.ndarray, k_blocks: Sequence[np.ndarray], v_blocks: Sequence[np.ndarray],
                  p: np.ndarray, c_blocks: Sequence[np.ndarray], order: Sequence[int], mask: str,
                  cu_seqlens=None, scale: Optional[float] = None):
-    """Online-softmax recurrence over K/V blocks visited in ``order``.
-
-    State: O = 0, m = -inf, l = 0.  Per block j: scores S = Q K_j^T * scale
-    (masked to -inf), m_j = rowmax(S), P = exp(S - m_j), l_j = rowsum(P);
-    m_new = max(m, m_j); O <- O exp(m - m_new) + (P V_j) exp(m_j - m_new);
-    l <- l exp(m - m_new) + l_j exp(m_j - m_new); m <- m_new.  At the end
-    O <- O / l.  Returns O [R,d], m, l [R].
-    """
+    """The online-softmax form over K/V blocks visited in ``order``: the
+    running state starts empty (O = 0, m = -inf, l = 0), each block's partial
+    state is folded into it with the merge rule, and the output is O / l
+    (compassingai.com page, section "線上 Softmax").  Returns O [R,d], m, l [R]."""
     q = np.asarray(q, dtype=np.float64)
     d = q.shape[-1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     R = q.shape[0]
-    O = np.zeros_like(q)
-    m = np.full(R, -np.inf)
-    l = np.zeros(R)
+    state = (np.zeros_like(q), np.full(R, -np.inf), np.zeros(R))
     for j in order:
-        k = np.asarray(k_blocks[j], np.float64)
-        v = np.asarray(v_blocks[j], np.float64)
-        S = np.where(visibility(p, c_blocks[j], mask, cu_seqlens), (q @ k.T) * scale, -np.inf)
-        m_j = S.max(axis=1) if S.shape[1] else np.full(R, -np.inf)
-        P = _exp_shift(S, m_j[:, None])
-        l_j = P.sum(axis=1)
-        m_new = np.maximum(m, m_j)
-        a_old = _exp_shift(m, m_new)
-        a_new = _exp_shift(m_j, m_new)
-        O = O * a_old[:, None] + (P @ v) * a_new[:, None]
-        l = l * a_old + l_j * a_new
-        m = m_new
+        state = _combine(state, _block_state(q, k_blocks[j], v_blocks[j], p, c_blocks[j], mask, cu_seqlens, scale))
+    O, m, l = state
     with np.errstate(invalid="ignore", divide="ignore"):
         O = np.where((l > 0)[:, None], O / np.where(l > 0, l, 1.0)[:, None], 0.0)
     return O, m, l

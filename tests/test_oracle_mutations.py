@@ -19,12 +19,12 @@ MUTATIONS = [
     ("doc_start", 'side="right"', 'side="left"'),
     ("rank_attention", "rank * L + rr", "rr"),
     ("block_partial", "c = j * L + np.arange", "c = rank * L + np.arange"),
-    ("online_merge", "O = O * a_old[:, None] + (P @ v) * a_new[:, None]",
-     "O = O + (P @ v) * a_new[:, None]"),
-    ("online_merge", "l = l * a_old + l_j * a_new", "l = l + l_j * a_new"),
+    ("_combine", "oa * wa[:, None] + ob * wb[:, None]", "oa + ob * wb[:, None]"),
+    ("_combine", "la * wa + lb * wb", "la + lb * wb"),
+    ("_block_state", "E.sum(axis=1)", "E.sum(axis=1) + 1e-9"),
     ("merge_lse", "w = _exp_shift(np.asarray(lse_parts[j], np.float64), lse)",
      "w = _exp_shift(lse, np.asarray(lse_parts[j], np.float64))"),
-    ("streaming_attention", "den += s.sum(axis=1)", "den += s.sum(axis=0).mean()"),
+    ("streaming_attention", "/ w.sum(axis=1)[:, None]", "/ w.sum(axis=0).mean()"),
     ("ring_schedule", "step = -1 if direction", "step = 1 if direction"),
     ("block_visible", "hi = np.minimum(p, (j + 1) * L - 1)", "hi = np.minimum(p, (j + 1) * L)"),
     ("visible_pairs", "np.sum(p - first + 1)", "np.sum(p - first)"),
