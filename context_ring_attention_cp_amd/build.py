@@ -43,26 +43,30 @@ COMMON = [
 ]
 
 
-# Placement of the bf16 block kernel's main loop (attn_mfma.hip): each form's
-# loop should start at this byte offset within a 32-byte instruction block
-# (16-28 run fastest on the full-block form; 20 measured best there, 24 on the
-# diagonal form).  The build reads where the loop lands and pads the kernel
-# entry with no-ops (CP_LOOP_PAD_<D>_<VT>) until it starts there.
-LOOP_FORMS = {(128, 1): 20, (128, 0): 24, (64, 1): 20, (64, 0): 20}
+# Placement of the block kernels' main loops (attn_mfma.hip, attn_fp8.hip):
+# each form's loop should start at the given byte offset within a 32-byte
+# instruction block.  For the bf16 kernel 16-28 ran fastest on the full-block
+# form (20 best; 24 on the diagonal form); for the FP8 kernel's full-block
+# form 28.  The build reads where each loop lands and pads the kernel entry
+# with no-ops (the file's pad macro for <D>_<VT>) until it starts there.
+PLACEMENT = {
+    "attn_mfma.hip": dict(kernel="attn_block_bf16_kernel", macro="CP_LOOP_PAD",
+                          forms={(128, 1): 20, (128, 0): 24, (64, 1): 20, (64, 0): 20}),
+    "attn_fp8.hip": dict(kernel="attn_block_fp8_kernel", macro="CP_F8_LOOP_PAD", forms={(128, 1): 28}),
+}
 LLVM = os.environ.get("ROCM_LLVM", "/opt/rocm/llvm/bin")
 
 
-def _pad_defs(pads: dict) -> list:
-    return [f"-DCP_LOOP_PAD_{d}_{vt}={k}" for (d, vt), k in pads.items()]
+def _pad_defs(src: str, pads: dict) -> list:
+    return [f"-D{PLACEMENT[src]['macro']}_{d}_{vt}={k}" for (d, vt), k in pads.items()]
 
 
-def _loop_offsets(pads: dict) -> dict:
+def _loop_offsets(src: str, pads: dict) -> dict:
     """Byte offset of each form's main loop (the backward branch spanning the
     most MFMAs) from its kernel's entry, for the given no-op pads."""
-    src = "attn_mfma.hip"
-    asm = os.path.join(BUILD, "placement.s")
-    obj = os.path.join(BUILD, "placement.o")
-    cmd = ([HIPCC] + COMMON + EXTRA.get(src, []) + _pad_defs(pads) +
+    asm = os.path.join(BUILD, f"placement_{src}.s")
+    obj = os.path.join(BUILD, f"placement_{src}.o")
+    cmd = ([HIPCC] + COMMON + EXTRA.get(src, []) + _pad_defs(src, pads) +
            ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -73,7 +77,7 @@ def _loop_offsets(pads: dict) -> dict:
                          capture_output=True, text=True, check=True).stdout
     out = {}
     for sec in dis.split("Disassembly of section")[1:]:
-        m = re.search(r"attn_block_bf16_kernelILi(\d+)ELb(\d)E", sec.split("\n")[0])
+        m = re.search(PLACEMENT[src]["kernel"] + r"ILi(\d+)ELb(\d)E", sec.split("\n")[0])
         if not m:
             continue
         insns = []   # (address, text)
@@ -94,23 +98,23 @@ def _loop_offsets(pads: dict) -> dict:
     return out
 
 
-def _placement_pads(verbose: bool) -> dict:
-    pads = {f: 0 for f in LOOP_FORMS}
+def _placement_pads(src: str, verbose: bool) -> dict:
+    forms = PLACEMENT[src]["forms"]
+    pads = {f: 0 for f in forms}
     for _ in range(6):
-        offs = _loop_offsets(pads)
-        off = {f: offs[f] % 32 for f in LOOP_FORMS}
-        if all(off[f] == LOOP_FORMS[f] for f in LOOP_FORMS):
+        offs = _loop_offsets(src, pads)
+        off = {f: offs[f] % 32 for f in forms}
+        if all(off[f] == forms[f] for f in forms):
             break
-        for f in LOOP_FORMS:
-            if off[f] != LOOP_FORMS[f]:
-                pads[f] = (pads[f] + ((LOOP_FORMS[f] - off[f]) % 32) // 4) % 8
+        for f in forms:
+            if off[f] != forms[f]:
+                pads[f] = (pads[f] + ((forms[f] - off[f]) % 32) // 4) % 8
     else:
-        bad = {f: o for f, o in off.items() if not 16 <= o <= 28}
-        if bad:
-            print(f"warning: main loop placement off target: {bad}", file=sys.stderr)
+        bad = {f: o for f, o in off.items() if o != forms[f]}
+        print(f"warning: {src}: main loop placement off target: {bad}", file=sys.stderr)
     if verbose:
-        print("main loop offsets mod 32: " + ", ".join(f"<{d},{bool(vt)}> {off[(d, vt)]} (pad {pads[(d, vt)]})"
-                                                        for d, vt in LOOP_FORMS))
+        print(f"{src}: main loop offsets mod 32: " +
+              ", ".join(f"<{d},{bool(vt)}> {off[(d, vt)]} (pad {pads[(d, vt)]})" for d, vt in forms))
     return pads
 
 
@@ -130,11 +134,11 @@ def _compile(src: str, defs: list = ()) -> str:
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        # the other sources compile while the bf16 kernel's loop placement is found
-        rest = {src: ex.submit(_compile, src) for src in SOURCES if src != "attn_mfma.hip"}
-        pads = _placement_pads(verbose)
-        objs = [_compile("attn_mfma.hip", _pad_defs(pads)) if src == "attn_mfma.hip" else rest[src].result()
-                for src in SOURCES]
+        # the other sources compile while the block kernels' loop placement is found
+        rest = {src: ex.submit(_compile, src) for src in SOURCES if src not in PLACEMENT}
+        placed = {src: ex.submit(lambda s: _compile(s, _pad_defs(s, _placement_pads(s, verbose))), src)
+                  for src in PLACEMENT}
+        objs = [(placed[src] if src in PLACEMENT else rest[src]).result() for src in SOURCES]
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

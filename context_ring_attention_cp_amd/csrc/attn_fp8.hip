@@ -81,8 +81,39 @@ __device__ __forceinline__ floatx16 mfma8(const int8v& a, const int8v& b, const 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// Code placement, as for the bf16 kernel: the build sets
+// CP_F8_LOOP_PAD_<D>_<VT>, the number of 4-byte no-ops at the kernel entry
+// that put the main loop at the offset within a 32-byte instruction block it
+// aims for (the full-block form ran 8.65 ms per launch at offset 28 against
+// 8.78-8.89 ms at the seven other offsets on one machine, two rounds; on a
+// faster machine offsets 4 and 28 were within 0.5 % of each other).
+#ifndef CP_F8_LOOP_PAD_128_1
+#define CP_F8_LOOP_PAD_128_1 0
+#endif
+#ifndef CP_F8_LOOP_PAD_128_0
+#define CP_F8_LOOP_PAD_128_0 0
+#endif
+#ifndef CP_F8_LOOP_PAD_64_1
+#define CP_F8_LOOP_PAD_64_1 0
+#endif
+#ifndef CP_F8_LOOP_PAD_64_0
+#define CP_F8_LOOP_PAD_64_0 0
+#endif
+#define CP_F8_STR2(x) #x
+#define CP_F8_STR(x) CP_F8_STR2(x)
+#define CP_F8_NOPS(n) asm volatile(".rept " CP_F8_STR(n) "\n s_nop 0\n .endr")
+
+template <int D, bool VT>
+__device__ __forceinline__ void loop_placement_fp8() {
+  if constexpr (D == 128 && VT) CP_F8_NOPS(CP_F8_LOOP_PAD_128_1);
+  else if constexpr (D == 128) CP_F8_NOPS(CP_F8_LOOP_PAD_128_0);
+  else if constexpr (VT) CP_F8_NOPS(CP_F8_LOOP_PAD_64_1);
+  else CP_F8_NOPS(CP_F8_LOOP_PAD_64_0);
+}
+
 template <int D, bool VT>
 __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
+  loop_placement_fp8<D, VT>();
   constexpr int CH = D / 16;         // 16-byte chunks per row
   constexpr int NS = D / 64;         // k-steps of S^T = K Q^T
   constexpr int NDT = D / 32;        // 32-row tiles of O^T
