@@ -210,8 +210,8 @@ def test_document_rows_per_step(cp, flags):
         _check_all(got, ref, "bf16")
 
 
-@pytest.mark.parametrize("L,d", [(1000, 128), (1243, 128), (1243, 64)])
-def test_key_split_diagonal(cp, L, d):
+@pytest.mark.parametrize("L,d,B", [(1000, 128, 1), (1243, 128, 1), (1243, 64, 1), (1243, 128, 2)])
+def test_key_split_diagonal(cp, L, d, B):
     """A causal shard whose diagonal launch fills the chip at most once runs
     the upper half of its query tiles as two workgroups each (the keys before
     and after the split point), and the next ring step merges the two running
@@ -220,16 +220,16 @@ def test_key_split_diagonal(cp, L, d):
     oracle; prefetch on and off bit-identical.  The workspace holds the side
     state exactly where the split applies."""
     N, H = 3, 3
-    spec = ShardSpec(S=N * L, N=N, H=H, d=d, dtype="bf16", mask="causal", cfg_id=140)
+    spec = ShardSpec(S=N * L, N=N, H=H, d=d, dtype="bf16", mask="causal", B=B, cfg_id=140)
     inp = make_inputs(spec, seed=13, ranks=range(N))
     kb, vb = _blocks(spec, inp)
-    side = 4 * L * H * d + 2 * 4 * H * L
-    base = cp.cp_attn_workspace_bytes(cp.Desc(1, H, d, N, L, 1, "bf16", "none"))
+    side = B * (4 * L * H * d + 2 * 4 * H * L)
+    base = cp.cp_attn_workspace_bytes(cp.Desc(B, H, d, N, L, 1, "bf16", "none"))
     assert cp.cp_attn_workspace_bytes(_desc(cp, spec, 1)) >= base + side
     assert cp.cp_attn_workspace_bytes(_desc(cp, spec, 0)) == base      # one step: no split
     for r in range(1, N):
         for fl, name in ((0, "forward"), (cp.CP_RING_REVERSE, "reverse")):
-            say(f"[key split] L={L} d={d} rank {r} {name}")
+            say(f"[key split] L={L} d={d} B={B} rank {r} {name}")
             q = dev(inp["q"][r], "bf16")
             got = run_rank(cp, spec, r, q, kb, vb, fl | cp.CP_RING_PREFETCH)
             serial = run_rank(cp, spec, r, q, kb, vb, fl)
