@@ -360,6 +360,36 @@ def test_full_size_rank_forward(cp, cfg):
     say(f"[full cfg {cfg}] {len(rows)} rows x {spec.H} heads: {stats}")
 
 
+@pytest.mark.parametrize("nqt", [512, 516])
+def test_document_order_at_and_past_its_table(cp, nqt):
+    """Under the document mask the host passes a launch's query-tile order
+    (by decreasing work) in the launch arguments, for up to 512 query tiles;
+    a launch with more tiles runs them in index order.  A 2-block ring of
+    ragged shards of exactly 512 and of 516 query tiles (L = 256 nqt - 37),
+    one head, documents of 500-9000 tokens, rank 1 with prefetch: sampled
+    rows (tile edges, document edges, a seeded set) against the oracle."""
+    N, H, d = 2, 1, 64
+    L = 256 * nqt - 37
+    S = N * L
+    rng = np.random.default_rng(41 + nqt)
+    pts = [0]
+    while pts[-1] < S:
+        pts.append(pts[-1] + int(rng.integers(500, 9000)))
+    cu = np.asarray(pts[:-1] + [S], np.int32)
+    spec = ShardSpec(S=S, N=N, H=H, d=d, dtype="bf16", mask="doc_causal", rank=1, cfg_id=141, cu_seqlens=cu)
+    blocks = [0, 1]
+    q, k, v = _full_inputs(spec, 0, blocks)
+    kb = [dev(k[j], "bf16") for j in blocks]
+    vb = [dev(v[j], "bf16") for j in blocks]
+    say(f"[document order] {nqt} query tiles, L={L}, {len(cu) - 1} documents")
+    got = run_rank(cp, spec, 1, dev(q, "bf16"), kb, vb, cp.CP_RING_PREFETCH)
+    extra = [t * 256 for t in range(nqt)][::16] + [x - L for x in cu if L <= x < 2 * L]
+    rows = sample_rows(L, nqt, n_random=96, extra=extra)
+    ref = oracle.rank_attention(q, k, v, 1, N, "doc_causal", cu, rows=rows, heads=[0])
+    stats = _check_all(got, ref, "bf16", rows=rows, heads=[0])
+    say(f"[document order] {len(rows)} rows: {stats}")
+
+
 def test_full_size_partial_merge(cp):
     """Bidirectional 64K over 8 ranks, rank 5, Q x 3: eight PARTIAL_LSE
     blocks, then merge_lse in a seeded shuffled order; sampled rows."""
