@@ -204,9 +204,11 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
     if (part == 2 && kt_begin < split_kt) kt_begin = split_kt;
   }
   const bool rd = a.flags & F_READ_STATE;
-  // nothing to compute and nothing to store: the state of these rows stays as it is
+  // nothing to compute and nothing to store: the state of these rows stays as
+  // it is (unless a side state waits to be merged into it)
   const bool wg_final = writes_final(a.flags, (q0 + BM < rows_end ? q0 + BM : rows_end) - 1, a.final_from);
-  if (kt_begin >= kt_end && rd && !wg_final && !(a.flags & F_WRITE_PARTIAL)) return;
+  const bool wg_side = (a.flags & F_READ_SIDE) && qt >= a.split_from;
+  if (kt_begin >= kt_end && rd && !wg_final && !wg_side && !(a.flags & F_WRITE_PARTIAL)) return;
 
   // This wave's rows.  Every wave runs every key tile of the workgroup; tiles
   // a wave cannot see are fully masked (only the few tiles of a causal
@@ -532,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_bf16_kernel(BlockArgs a) 
   }
 
   if (!row_ok || qrow >= rows_end) return;
-  if ((a.flags & F_READ_SIDE) && qt >= a.split_from) {
+  if (wg_side) {
     // the other key range of a split tile: merge the two states at their common max
     const float m2 = a.side_m[ml_idx] * kLog2e;
     const float mt = fmaxf(m_true, m2);
