@@ -15,12 +15,17 @@ readings below are this library's choices:
 * format: OCP FP8 E4M3 (1 sign bit, 4 exponent bits with bias 7, 3 mantissa
   bits, largest finite value 448, no infinities), the format of the
   matrix-core FP8 inputs on MI355X;
-* scaling: one scale per (batch, head) and tensor block: amax is the largest
-  |x| over the block's tokens and head dim, scale = amax / 448 and
-  inv = 448 / amax (both float32, correctly rounded; scale = inv = 1 when
-  amax = 0); the code of x is the e4m3 value nearest to
-  clamp(float32(x) * inv, -448, 448), ties to the even code; the value it
-  stands for is decode(code) * scale;
+* scaling: one scale per (batch, head) and tensor block, a power of two.
+  With y = float32(x * c), where c = 1 for keys and values and, for the
+  query, c is the softmax scale times log2(e) in float32 (``query_prescale``),
+  amax is the largest |y| over the block's tokens and head dim and
+  scale = 2^e, e the smallest integer >= -126 with amax <= 448 * 2^e
+  (e = 0 when amax = 0); the code of x is the e4m3 value nearest to
+  y * 2^-e (at most 448 in magnitude by the choice of e), ties to the even
+  code, and it stands for decode(code) * scale / c.  Powers of two are what
+  the matrix core's block-scale operands apply exactly, and with c folded
+  into the query the products of query and key codes come out as base-2
+  logits;
 * attention: the forward of the shard (oracle ``attention.rank_attention``)
   on the dequantised Q, K and V, computed in float64.  The GPU kernel also
   rounds P to e4m3 for the P V product; that is an approximation of this
@@ -29,6 +34,7 @@ readings below are this library's choices:
 
 Functions: ``e4m3_values`` (the value table), ``e4m3_decode``,
 ``e4m3_encode`` (nearest value, ties to even, over the finite codes),
+``query_prescale`` (c of the query), ``scale_exponent`` (e of an amax),
 ``quantize_heads`` (scale and codes of a [B, L, H, d] block),
 ``dequantize_heads``, ``fp8_rank_attention``.
 """
@@ -40,10 +46,11 @@ import numpy as np
 
 from . import attention as fwd
 
-__all__ = ["E4M3_MAX", "e4m3_values", "e4m3_decode", "e4m3_encode", "quantize_heads", "dequantize_heads",
-           "fp8_rank_attention"]
+__all__ = ["E4M3_MAX", "LOG2E", "e4m3_values", "e4m3_decode", "e4m3_encode", "query_prescale", "scale_exponent",
+           "quantize_heads", "dequantize_heads", "fp8_rank_attention"]
 
 E4M3_MAX = 448.0
+LOG2E = 1.4426950408889634        # log2(e), rounded to float32 where it is used
 
 
 def e4m3_values() -> np.ndarray:
@@ -86,32 +93,60 @@ def e4m3_encode(x) -> np.ndarray:
     return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
 
 
-def quantize_heads(x) -> Dict[str, np.ndarray]:
+def query_prescale(d: int, scale: Optional[float] = None) -> np.float32:
+    """c of the query: float32(s * float32(log2 e)), with s = float32(scale),
+    or float32(1 / float32(sqrt(d))) when scale is None or not positive; each
+    operation rounded to float32."""
+    if scale is None or scale <= 0:
+        s = np.float32(1) / np.sqrt(np.float32(d))
+    else:
+        s = np.float32(scale)
+    return np.float32(np.float32(s) * np.float32(LOG2E))
+
+
+def scale_exponent(amax) -> np.ndarray:
+    """e of each amax: the smallest integer >= -126 with amax <= 448 * 2^e
+    (0 where amax == 0), found by counting up from -126; the comparisons are
+    exact in float64."""
+    a = np.asarray(amax, dtype=np.float64)
+    out = np.zeros(a.shape, dtype=np.int64)
+    for idx, v in np.ndenumerate(a):
+        if v > 0:
+            e = -126
+            while v > E4M3_MAX * 2.0 ** e:
+                e += 1
+            out[idx] = e
+    return out
+
+
+def quantize_heads(x, prescale=1.0) -> Dict[str, np.ndarray]:
     """Scale and codes of a block x [B, L, H, d] (float32 values, e.g. the
-    bf16 inputs): per (b, h) amax over tokens and head dim; returns
-    ``codes`` [B, L, H, d] uint8 and ``scale`` [B, H] float32 (amax / 448)."""
+    bf16 inputs) multiplied by ``prescale`` (c): per (b, h) amax of
+    y = float32(x * c) over tokens and head dim; returns ``codes``
+    [B, L, H, d] uint8 and ``scale`` [B, H] float32 (2^e)."""
     x = np.asarray(x, dtype=np.float32)
-    amax = np.abs(x).max(axis=(1, 3))                      # [B, H], exact
-    zero = amax == 0
-    safe = np.where(zero, np.float32(1), amax).astype(np.float32)
-    scale = np.where(zero, np.float32(1), safe / np.float32(E4M3_MAX)).astype(np.float32)
-    inv = np.where(zero, np.float32(1), np.float32(E4M3_MAX) / safe).astype(np.float32)
-    y = (x * inv[:, None, :, None]).astype(np.float32)     # one float32 rounding, as on the GPU
-    y = np.clip(y, -E4M3_MAX, E4M3_MAX)
-    return {"codes": e4m3_encode(y), "scale": scale.astype(np.float32)}
+    y = (x * np.float32(prescale)).astype(np.float32)      # one float32 rounding (none when c = 1)
+    amax = np.abs(y).max(axis=(1, 3))                      # [B, H], exact
+    e = scale_exponent(amax)
+    scale = np.exp2(e.astype(np.float64)).astype(np.float32)
+    z = y.astype(np.float64) * np.exp2(-e.astype(np.float64))[:, None, :, None]   # exact
+    z = np.clip(z, -E4M3_MAX, E4M3_MAX)
+    return {"codes": e4m3_encode(z), "scale": scale}
 
 
-def dequantize_heads(codes, scale) -> np.ndarray:
-    """float64 values decode(code) * scale, [B, L, H, d]."""
-    return e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[:, None, :, None]
+def dequantize_heads(codes, scale, prescale=1.0) -> np.ndarray:
+    """float64 values decode(code) * scale / c, [B, L, H, d]."""
+    return e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[:, None, :, None] / float(prescale)
 
 
 def fp8_rank_attention(q_codes, q_scale, k_codes: Sequence, k_scales: Sequence, v_codes: Sequence,
                        v_scales: Sequence, rank: int, N: int, mask: str, cu_seqlens=None,
-                       scale: Optional[float] = None, rows=None, heads=None) -> Dict[str, np.ndarray]:
-    """The shard's forward on the dequantised inputs (float64); blocks not
-    supplied (None) must be invisible to the shard, as in ``rank_attention``."""
-    q = dequantize_heads(q_codes, q_scale)
+                       scale: Optional[float] = None, rows=None, heads=None,
+                       q_prescale=1.0) -> Dict[str, np.ndarray]:
+    """The shard's forward on the dequantised inputs (float64), the query's
+    codes standing for decode * q_scale / q_prescale; blocks not supplied
+    (None) must be invisible to the shard, as in ``rank_attention``."""
+    q = dequantize_heads(q_codes, q_scale, q_prescale)
     ks = {j: dequantize_heads(k_codes[j], k_scales[j]) for j in range(N) if k_codes[j] is not None}
     vs = {j: dequantize_heads(v_codes[j], v_scales[j]) for j in range(N) if v_codes[j] is not None}
     return fwd.rank_attention(q, ks, vs, rank, N, mask, cu_seqlens, scale, rows=rows, heads=heads)

@@ -2,8 +2,13 @@
 brute-force round-to-nearest-even, the quantisation's defining properties
 and the plain definition on exactly representable inputs
 (tests/oracle_fp8_pins.py); and planted mistakes the pins must catch: a
-wrong exponent bias, ties rounded away from even, a wrong scale constant,
-one scale for all heads, a double-rounded inverse scale, a missing clamp."""
+wrong exponent bias, ties rounded away from even, a lost sign of zero, a
+scale exponent for the largest value 240 (the fnuz variant), a boundary
+compared the wrong way, the clamp at -126 lost, a zero block given a
+nonzero exponent, a wrong log2(e) or sqrt, one scale for all
+heads, the query's c ignored or applied without the float32 rounding, codes
+off by a factor of two, and a dequantisation that multiplies where it
+divides."""
 import inspect
 import textwrap
 
@@ -24,12 +29,19 @@ MUTATIONS = [
     ("e4m3_encode", "((d_hi == d_lo) & (hi % 2 == 0))", "((d_hi == d_lo))"),
     ("e4m3_encode", "return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)",
      "return (code | np.where(np.signbit(x) & (code != 0), 0x80, 0)).astype(np.uint8)"),
-    ("quantize_heads", "safe / np.float32(E4M3_MAX)", "safe / np.float32(256.0)"),
-    ("quantize_heads", "amax = np.abs(x).max(axis=(1, 3))", "amax = np.abs(x).max(axis=(1, 3)) * 0 + np.abs(x).max()"),
-    ("quantize_heads", "inv = np.where(zero, np.float32(1), np.float32(E4M3_MAX) / safe).astype(np.float32)",
-     "inv = np.where(zero, np.float32(1), np.float32(1) / scale).astype(np.float32)"),
-    ("quantize_heads", "y = np.clip(y, -E4M3_MAX, E4M3_MAX)", "y = y * np.float32(1.001)"),
+    ("scale_exponent", "while v > E4M3_MAX * 2.0 ** e:", "while v > 240.0 * 2.0 ** e:"),
+    ("scale_exponent", "while v > E4M3_MAX * 2.0 ** e:", "while v >= E4M3_MAX * 2.0 ** e:"),
+    ("scale_exponent", "e = -126", "e = -127"),
+    ("scale_exponent", "if v > 0:", "if v >= 0:"),
+    ("query_prescale", "np.float32(LOG2E)", "np.float32(1.4427)"),
+    ("query_prescale", "np.float32(1) / np.sqrt(np.float32(d))", "np.float32(1) / np.float32(np.sqrt(float(d)) * 1.0000001)"),
+    ("quantize_heads", "amax = np.abs(y).max(axis=(1, 3))", "amax = np.abs(y).max(axis=(1, 3)) * 0 + np.abs(y).max()"),
+    ("quantize_heads", "y = (x * np.float32(prescale)).astype(np.float32)", "y = x.astype(np.float32)"),
+    ("quantize_heads", "y = (x * np.float32(prescale)).astype(np.float32)",
+     "y = (x.astype(np.float64) * float(np.float32(prescale)))"),
+    ("quantize_heads", "np.exp2(-e.astype(np.float64))", "np.exp2(-e.astype(np.float64) - 1)"),
     ("dequantize_heads", "e4m3_decode(codes) * np.asarray(scale", "e4m3_decode(codes) / np.asarray(scale"),
+    ("dequantize_heads", "/ float(prescale)", "* float(prescale)"),
 ]
 
 
