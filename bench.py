@@ -477,11 +477,11 @@ def fp8_forward(cp, spec, seed: int, cs, xs, reps: int) -> dict:
     qd1 = cp.Desc(spec.B, spec.H, spec.d, 1, spec.L, 0, "bf16", "none")
     codes, scales = [], []
     x = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
-    for _ in range(1 + 2 * spec.N):
+    for i in range(1 + 2 * spec.N):          # the query (with the softmax's base-2 factor), then K and V blocks
         x.copy_(torch.randn(shape, generator=gen, device="cuda"))
         c = torch.empty(shape, dtype=torch.uint8, device="cuda")
         sc = torch.empty((spec.B, spec.H), device="cuda")
-        cp.cp_attn_quantize_fp8(qd1, x, c, sc)
+        cp.cp_attn_quantize_fp8(qd1, x, c, sc, role=cp.CP_FP8_QUERY if i == 0 else cp.CP_FP8_KV)
         codes.append(c)
         scales.append(sc)
     ms_q = _timed(lambda: cp.cp_attn_quantize_fp8(qd1, x, codes[-1], scales[-1], stream=cs), cs, 2, reps)
@@ -515,7 +515,8 @@ def fp8_forward(cp, spec, seed: int, cs, xs, reps: int) -> dict:
     assert torch.isfinite(o.float()).all(), "non-finite FP8 output"
     fl = attn_flops(spec, cp.cp_attn_visible_pairs(desc))
     k_tf = fl * reps / (sum(kms) * 1e-3) / 1e12
-    res = {"workload": "causal last-rank shard of the 128K example with e4m3 Q/K/V (per-(batch, head) scales), "
+    res = {"workload": "causal last-rank shard of the 128K example with e4m3 Q/K/V (per-(batch, head) power-of-two "
+                       "scales), "
                        "bf16 output: S=131072 N=4 L=32768 rank=3 B=1 H=32 d=128, ring prefetch",
            "blocks": sched, "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
            "kernel_mean_ms": round(sum(kms) / max(1, len(kms)), 4), "kernel_tflops": round(k_tf, 2),

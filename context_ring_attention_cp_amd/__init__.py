@@ -5,7 +5,8 @@ in include/cpattn.h).  The binding only marshals arguments; every step of the
 computation runs in the library's kernels.
 """
 from ._binding import (  # noqa: F401
-    CP_BF16, CP_ERR_HIP, CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED, CP_ERR_WORKSPACE, CP_F32, CP_MASK_CAUSAL,
+    CP_BF16, CP_ERR_HIP, CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED, CP_ERR_WORKSPACE, CP_F32, CP_FP8_KV, CP_FP8_QUERY,
+    CP_MASK_CAUSAL,
     CP_MASK_DOC_CAUSAL, CP_MASK_NONE, CP_MAX_RING, CP_MODE_ACCUMULATE, CP_MODE_INIT, CP_MODE_PARTIAL_LSE,
     CP_OK, CP_RING_PREFETCH, CP_RING_REVERSE, CP_STATIC_SCRATCH_BYTES, EXPORTED, CpAttnError, Desc, Profiler, cp_attn_block_backward,
     cp_attn_block_partial, cp_attn_bwd_delta, cp_attn_finalize, cp_attn_measure_lds_stream, cp_attn_merge_lse, cp_attn_quantize_fp8,

@@ -23,6 +23,7 @@ CP_F32, CP_BF16 = 0, 1
 CP_MODE_INIT, CP_MODE_ACCUMULATE, CP_MODE_PARTIAL_LSE = 0, 1, 2
 CP_RING_PREFETCH, CP_RING_REVERSE = 1, 2
 CP_MAX_RING = 64
+CP_FP8_KV, CP_FP8_QUERY = 0, 1
 CP_STATIC_SCRATCH_BYTES = 96 << 20
 
 MASKS = {"none": CP_MASK_NONE, "causal": CP_MASK_CAUSAL, "doc_causal": CP_MASK_DOC_CAUSAL}
@@ -100,7 +101,7 @@ def lib() -> ctypes.CDLL:
         L.cp_attn_ulysses_workspace_bytes.restype = ctypes.c_size_t
         L.cp_attn_ulysses_forward.argtypes = [dp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                               ctypes.POINTER(vp), f32p, f32p, f32p, vp, ctypes.c_size_t, vp]
-        L.cp_attn_quantize_fp8.argtypes = [dp, vp, vp, f32p, vp]
+        L.cp_attn_quantize_fp8.argtypes = [dp, vp, ctypes.c_int32, vp, f32p, vp]
         L.cp_attn_rank_forward_fp8.argtypes = [dp, vp, f32p, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                                ctypes.POINTER(vp), ctypes.POINTER(vp), vp, f32p, f32p, f32p, vp,
                                                ctypes.c_size_t, vp, vp, i32, vp]
@@ -353,8 +354,10 @@ def cp_attn_ulysses_forward(desc: Desc, q_shards: Sequence, k_shards: Sequence, 
                                          workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
-def cp_attn_quantize_fp8(desc: Desc, x, codes, scales, stream=None) -> None:
-    """x: bf16 [B, L, H, d]; codes: uint8 [B, L, H, d]; scales: float32 [B, H]."""
+def cp_attn_quantize_fp8(desc: Desc, x, codes, scales, stream=None, role: int = CP_FP8_KV) -> None:
+    """x: bf16 [B, L, H, d]; codes: uint8 [B, L, H, d]; scales: float32 [B, H];
+    role CP_FP8_KV (keys, values) or CP_FP8_QUERY (the query, with the
+    softmax's base-2 factor folded in, as cp_attn_rank_forward_fp8 expects)."""
     import torch
     c = desc.c
     big = (c.B, c.L, c.H, c.d)
@@ -363,7 +366,7 @@ def cp_attn_quantize_fp8(desc: Desc, x, codes, scales, stream=None) -> None:
     _check_tensor(scales, "scales", (c.B, c.H), torch.float32)
     if codes is None or scales is None:
         raise ValueError("codes and scales are required")
-    _check(lib().cp_attn_quantize_fp8(desc.ref, _ptr(x), _ptr(codes), _ptr(scales), _stream(stream)))
+    _check(lib().cp_attn_quantize_fp8(desc.ref, _ptr(x), int(role), _ptr(codes), _ptr(scales), _stream(stream)))
 
 
 def cp_attn_rank_forward_fp8(desc: Desc, q, q_scale, k_blocks: Sequence, k_scales: Sequence, v_blocks: Sequence,

@@ -1003,11 +1003,13 @@ cp_status cp_attn_ulysses_forward(const cp_attn_desc* desc, const void* const* q
   return CP_OK;
 }
 
-cp_status cp_attn_quantize_fp8(const cp_attn_desc* desc, const void* x, void* codes, float* scales, void* stream) {
+cp_status cp_attn_quantize_fp8(const cp_attn_desc* desc, const void* x, int32_t role, void* codes, float* scales,
+                               void* stream) {
   g_last_error.clear();
   cp_status st = check_desc(desc);
   if (st != CP_OK) return st;
   if (desc->dtype != CP_BF16) return fail(CP_ERR_UNSUPPORTED, "cp_attn_quantize_fp8 takes bf16 input (dtype=%d)", desc->dtype);
+  if (role != CP_FP8_KV && role != CP_FP8_QUERY) return fail(CP_ERR_INVALID_ARG, "unknown FP8 role %d", role);
   if ((st = check_tensor(x, "x")) != CP_OK) return st;
   if (!codes) return fail(CP_ERR_INVALID_ARG, "codes is NULL");
   if (!aligned(codes, 8)) return fail(CP_ERR_INVALID_ARG, "codes is not 8-byte aligned");
@@ -1021,7 +1023,8 @@ cp_status cp_attn_quantize_fp8(const cp_attn_desc* desc, const void* x, void* co
   a.L = desc->L;
   a.B = desc->B;
   a.H = desc->H;
-  const hipError_t e = launch_quantize_fp8(a, desc->d, (hipStream_t)stream);
+  const float prescale = role == CP_FP8_QUERY ? scale_log2(desc) : 1.0f;
+  const hipError_t e = launch_quantize_fp8(a, desc->d, prescale, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "quantisation launch");
   return CP_OK;
 }

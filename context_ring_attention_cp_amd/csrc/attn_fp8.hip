@@ -1,6 +1,7 @@
 // FP8 (OCP e4m3) block kernel for gfx950: one rank's query shard against one
-// K/V block, Q, K and V given as e4m3 codes with one float32 scale per
-// (batch, head) each (value = decode(code) * scale), the output in bf16.
+// K/V block, Q, K and V given as e4m3 codes with one power-of-two float32
+// scale per (batch, head) each (value = decode(code) * scale; the query's
+// codes also carry the softmax scale times log2(e)), the output in bf16.
 //
 // The recurrence, work split, wave ping-pong, LDS ring, fetch schedule, masks
 // and lazy rescaling are those of the bf16 kernel (attn_mfma.hip); the online
@@ -30,9 +31,20 @@
 //   operand consumes them (key 16 q + 8 g + e at position 32 g + 8 q + e), so
 //   the 32 bytes of lane half g are contiguous: two 16-byte LDS reads per
 //   operand instead of four transpose loads.
-// Scales: S = s_q s_k (codes product), folded into the exp2 coefficient; the
+// Scales: the S^T products run as v_mfma_scale_f32_32x32x64_f8f6f4 with the
+//   key block's and the query's exponents as the e8m0 block scales (powers
+//   of two, applied exactly), and the query's codes already hold the softmax
+//   scale times log2(e): the accumulators are the base-2 logits x.  The O
 //   accumulator holds sum P V_codes, so the running state is divided by s_v
 //   on load and O multiplied by s_v before it is stored.
+// P = exp2(x - m_ref) with an integer reference m_ref: v_exp_f32 of x itself,
+//   and the e4m3 conversion v_cvt_scalef32_pk_fp8_f32 divides by 2^m_ref
+//   (it uses the exponent of its scale operand; both steps exact as powers of
+//   two), so the softmax issues no multiply-add per score.  That needs
+//   2^(m_ref + 8) and 2^(m_ref - 10) to be normal float32 values (P below
+//   2^-10 rounds to code 0 either way): for -116 <= m_ref <= 119 in every
+//   lane of the wave; otherwise the wave subtracts m_ref first and converts
+//   with scale 1.
 // P is rounded to e4m3 for the PV product (P <= 256 under the lazy rescale, so
 //   it never reaches the 448 limit); l sums the same rounded values, so O / l
 //   stays a convex combination of V rows.  The row sums come from the matrix
@@ -60,6 +72,7 @@ template <int V> struct Tag { static constexpr int value = V; };
 
 typedef int int8v __attribute__((ext_vector_type(8)));
 typedef int int2v __attribute__((ext_vector_type(2)));
+typedef short short2v __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -80,6 +93,15 @@ template <int D> __device__ __forceinline__ int swz8(int row) {
 __device__ __forceinline__ floatx16 mfma8(const int8v& a, const int8v& b, const floatx16& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
+
+// The same product scaled by 2^(byte 0 of sc - 127) for A and 2^(byte 1 of
+// sc - 127) for B (e8m0 block scales, one register for both).
+__device__ __forceinline__ floatx16 mfma8_scaled(const int8v& a, const int8v& b, const floatx16& c, int sc) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sc, 1, sc);
+}
+
+// e8m0 code of a power-of-two float32 (its biased exponent)
+__device__ __forceinline__ int e8m0_of(float s) { return (int)((__float_as_uint(s) >> 23) & 0xFF); }
 
 // Code placement, as for the bf16 kernel: the build sets
 // CP_F8_LOOP_PAD_<D>_<VT>, the number of 4-byte no-ops at the kernel entry
@@ -150,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
   const int64_t nkt_all = (L + BN - 1) / BN;
   const uint8_t* __restrict__ vg = (const uint8_t*)a.v + (VT ? ((int64_t)b * H + h) * D * nkt_all * BN : base);
   const int bh = b * H + h;
-  const float s_qk = a.q_scale[bh] * a.k_scale[bh];
+  const int sc_kq = e8m0_of(a.k_scale[bh]) | (e8m0_of(a.q_scale[bh]) << 8);
   const float s_v = a.v_scale[bh];
 
   const int64_t q0 = (int64_t)qt * BM;
@@ -202,7 +224,8 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
   }
 
   // Running state (base-2 units; the O accumulator in units of s_v; every
-  // element of lacc holds the row sum l of this lane's query).
+  // element of lacc holds the row sum l of this lane's query).  O and l are
+  // relative to m_ref, an integer (or -inf) at least as large as m_true.
   floatx16 oacc[NDT];
   floatx16 lacc = floatx16{};
   float m_true = -INFINITY, m_ref = -INFINITY;
@@ -211,9 +234,13 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = floatx16{};
   if (rd && row_ok) {
-    const float inv_v = 1.f / s_v;
-    m_true = m_ref = a.st_m[ml_idx] * kLog2e;
-    const float l0 = a.st_l[ml_idx];
+    // the stored state is relative to the true running max: move it to the
+    // integer reference above it
+    m_true = a.st_m[ml_idx] * kLog2e;
+    m_ref = ceilf(m_true);
+    const float f = m_true == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_true - m_ref);
+    const float fv = f / s_v;
+    const float l0 = a.st_l[ml_idx] * f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) lacc[i] = l0;
 #pragma unroll
@@ -221,14 +248,12 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const float4 v4 = *(const float4*)(a.st_o + st_row + 32 * dt + 8 * i4 + 4 * g);
-        oacc[dt][4 * i4 + 0] = v4.x * inv_v;
-        oacc[dt][4 * i4 + 1] = v4.y * inv_v;
-        oacc[dt][4 * i4 + 2] = v4.z * inv_v;
-        oacc[dt][4 * i4 + 3] = v4.w * inv_v;
+        oacc[dt][4 * i4 + 0] = v4.x * fv;
+        oacc[dt][4 * i4 + 1] = v4.y * fv;
+        oacc[dt][4 * i4 + 2] = v4.z * fv;
+        oacc[dt][4 * i4 + 3] = v4.w * fv;
       }
   }
-
-  const float c2 = a.scale_log2 * s_qk;
 
   // Tile fetch by the 256 lanes of waves 0-3: fetch i of a lane fills 16-byte
   // slot (i * 256 + tid) of the tile, row i * RPS + tid / CH, physical chunk
@@ -337,7 +362,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
 #pragma unroll
     for (int j = J0; j < J1; ++j) {
       const int8v op = ring[(j - J0) % RA];
-      if (j < NQK) sacc[j % NT] = mfma8(op, qreg[j / NT], sacc[j % NT]);
+      if (j < NQK) sacc[j % NT] = mfma8_scaled(op, qreg[j / NT], sacc[j % NT], sc_kq);
       else oacc[(j - NQK) % NDT] = mfma8(op, pb[(j - NQK) / NDT], oacc[(j - NQK) % NDT]);
       if (j + RA < J1) ring[(j - J0) % RA] = rd(j + RA);
       __builtin_amdgcn_sched_barrier(0);
@@ -349,6 +374,12 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
         lacc = mfma8(int8v{kOne, kOne, kOne, kOne, kOne, kOne, kOne, kOne}, pb[kh], lacc);
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    if constexpr (QK) {
+      // The scaled products are otherwise sunk past the phase's end to their
+      // first use; an (empty) use here keeps them in the compute phase.
+#pragma unroll
+      for (int t = 0; t < NT; ++t) asm volatile("" ::"v"(sacc[t]));
     }
   };
 
@@ -396,39 +427,49 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
     const float mx = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
     return fmaxf(mx, xor32(mx));
   };
-  auto rescale = [&](float mx) {
-    const float mt = mx * c2;
-    m_true = fmaxf(m_true, mt);
-    const bool need = mt > m_ref + kLazy;
-    if (__any(need)) {
-      const float nref = need ? m_true : m_ref;
+  // The lazy rescale, and the reference the exponentials use.  Returns the
+  // scale operand of the e4m3 conversions: 2^m_ref when every lane's
+  // reference is in the range where exp2(x) and 2^m_ref are normal floats;
+  // otherwise the wave subtracts m_ref from the logits here and converts with
+  // scale 1.  Both rare cases share one branch.
+  auto rescale = [&](float mx, floatx16 (&sacc)[NT]) -> float {
+    m_true = fmaxf(m_true, mx);
+    const bool need = mx > m_ref + kLazy;
+    const float nref = need ? ceilf(m_true) : m_ref;
+    const float m_use = nref == -INFINITY ? 0.f : nref;
+    const bool fast = __all(m_use >= -116.f && m_use <= 119.f);
+    if (__any(need) || !fast) {
       const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - nref) : 1.f;
-      m_ref = nref;
       lacc *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+      if (!fast) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) sacc[t] -= m_use;
+      }
     }
+    m_ref = nref;
+    return fast ? __uint_as_float((uint32_t)((int)m_use + 127) << 23) : 1.f;
   };
   // P = exp2(x - m_ref), rounded to e4m3 as the PV B operands (operand h:
-  // bytes 0-15 from sub-tile 2h, 16-31 from sub-tile 2h+1).
-  auto exp_sum = [&](floatx16 (&sacc)[NT], int8v (&pb)[NH]) {
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+  // bytes 0-15 from sub-tile 2h, 16-31 from sub-tile 2h+1).  The first
+  // conversion of a word keeps bytes 2-3 of its old value, which the second
+  // one overwrites.  Passing the previous tile's word (already consumed by the
+  // P V products of this step's compute phase) keeps the conversions in place
+  // in the operand registers.
+  auto exp_sum = [&](floatx16 (&sacc)[NT], int8v (&pb)[NH], float pscale) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][i], c2, -m_use));
+      for (int i = 0; i < 16; ++i) sacc[t][i] = __builtin_amdgcn_exp2f(sacc[t][i]);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        // The first conversion keeps bytes 2-3 of its third operand, which the
-        // second one overwrites.  Passing the previous tile's word (already
-        // consumed by the P V products of this step's compute phase) keeps the
-        // conversions in place in the operand registers.
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[t][4 * q], sacc[t][4 * q + 1], pb[t / 2][4 * (t % 2) + q],
-                                                   false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[t][4 * q + 2], sacc[t][4 * q + 3], word, true);
-        pb[t / 2][4 * (t % 2) + q] = word;
+        short2v w2 = __builtin_bit_cast(short2v, pb[t / 2][4 * (t % 2) + q]);
+        w2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w2, sacc[t][4 * q], sacc[t][4 * q + 1], pscale, false);
+        w2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w2, sacc[t][4 * q + 2], sacc[t][4 * q + 3], pscale, true);
+        pb[t / 2][4 * (t % 2) + q] = __builtin_bit_cast(int, w2);
       }
   };
 
@@ -456,8 +497,8 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
       }
       if constexpr (QK) {
         if (need_mask(u)) apply_mask(u, sacc);
-        rescale(row_max(sacc));
-        exp_sum(sacc, pb);
+        const float pscale = rescale(row_max(sacc), sacc);
+        exp_sum(sacc, pb, pscale);
       }
       // tile u+1 must have landed: at most the fetch of tile u+2 (2 DMA tensors) outstanding
       __asm__ volatile("" ::: "memory");
@@ -486,7 +527,7 @@ __global__ __launch_bounds__(kThreads) void attn_block_fp8_kernel(BlockArgs a) {
   const float l_tot = lacc[0];
   const bool has = l_tot > 0.f;
   const float m_run = m_true;
-  // m in natural-log units of the true scores (c2 includes the FP8 scales)
+  // m in natural-log units of the true scores (x is the base-2 logit)
   if (writes_state(a.flags, qrow, a.final_from)) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)

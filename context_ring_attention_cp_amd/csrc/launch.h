@@ -55,7 +55,8 @@ hipError_t launch_a2a_scatter(const RegroupArgs& a, hipStream_t s);
 // The gather of bf16 V straight into the tiled layout F_V_TILED reads, over the
 // whole sequence: full = [B, Hn, S / 64, d, 64]; S a multiple of 64.
 hipError_t launch_a2a_gather_v_tiles(const RegroupArgs& a, hipStream_t s);
-hipError_t launch_quantize_fp8(const QuantArgs& a, int d, hipStream_t s);
+// x is multiplied by prescale (float32) before it is quantised.
+hipError_t launch_quantize_fp8(const QuantArgs& a, int d, float prescale, hipStream_t s);
 // FP8 (e4m3) inputs, bf16 output; the same flags and state as the bf16 kernel.
 hipError_t launch_block_fp8(const BlockArgs& a, int d, hipStream_t s, const LaunchEvents& ev = {});
 // Measurement: read `bytes` (a multiple of 4096) from src through the

@@ -252,27 +252,39 @@ cp_status cp_attn_ulysses_forward(const cp_attn_desc* desc, const void* const* q
  * The compassingai.com page notes that the bytes CP moves depend on whether
  * blocks travel compressed or in FP8 (section "通訊量分析") and that
  * FlashAttention-3 computes attention in FP8 (section "技術演進史").  This
- * library's FP8 format is OCP E4M3 (largest value 448) with one float32 scale
- * per (batch, head) and block: scale = amax / 448 over the block's tokens and
- * head dim, inverse 448 / amax (both correctly rounded; 1 when amax = 0); a
- * value x is stored as the e4m3 code nearest to clamp(x * inverse, +-448),
- * ties to even, and stands for decode(code) * scale. */
+ * library's FP8 format is OCP E4M3 (largest value 448) with one float32
+ * scale per (batch, head) and block, a power of two: with y = float32(x * c)
+ * (c = 1 for keys and values; for the query, c = the desc's softmax scale
+ * times log2(e), rounded to float32), amax = max |y| over the block's tokens
+ * and head dim and scale = 2^e, e the smallest integer >= -126 with
+ * amax <= 448 * 2^e (0 when amax = 0).  A value x is stored as the e4m3 code
+ * nearest to y * 2^-e, ties to even, and stands for decode(code) * scale / c.
+ * Power-of-two scales are applied exactly by the FP8 matrix core's block-scale
+ * operands, and the query's c makes its products with the key codes base-2
+ * logits. */
+#define CP_FP8_KV 0     /* role of a key or value block: c = 1 */
+#define CP_FP8_QUERY 1  /* role of the query: c = softmax scale * log2(e) */
 
 /* Quantise one bf16 block x (device [B, L, H, d] with desc's B, L, H, d) to
  * codes (device [B, L, H, d] bytes, 8-byte aligned) and scales (device [B, H]
- * float32).  x must be finite.  Four launches on stream (fill, per-head
- * maxima, codes, scales); scales is overwritten.
- * Errors: CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED (desc->dtype not bf16), CP_ERR_HIP. */
-cp_status cp_attn_quantize_fp8(const cp_attn_desc* desc, const void* x, void* codes, float* scales, void* stream);
+ * float32) in the given role (CP_FP8_KV or CP_FP8_QUERY; the query's c uses
+ * desc->scale, 1/sqrt(d) when 0).  x must be finite.  Four launches on stream
+ * (fill, per-head maxima, codes, scales); scales is overwritten.
+ * Errors: CP_ERR_INVALID_ARG (also an unknown role), CP_ERR_UNSUPPORTED
+ * (desc->dtype not bf16), CP_ERR_HIP. */
+cp_status cp_attn_quantize_fp8(const cp_attn_desc* desc, const void* x, int32_t role, void* codes, float* scales,
+                               void* stream);
 
 /* The whole forward of rank desc->rank over the simulated ring, as
  * cp_attn_rank_forward, with FP8 inputs: q (device [B, L, H, d] e4m3 codes)
  * with q_scale (device [B, H] float32), and per block j the codes k_blocks[j],
  * v_blocks[j] with k_scales[j], v_scales[j] (HOST arrays of N device
  * pointers; entries of blocks the rank never visits may be NULL), all as
- * written by cp_attn_quantize_fp8 (scales must be finite and positive; they
- * live in device memory and are not checked).  The ring moves the one-byte codes (half
- * the bytes of bf16).  Both products run on the FP8 matrix cores with float32
+ * written by cp_attn_quantize_fp8: q in the CP_FP8_QUERY role under a desc
+ * with this desc's scale, the blocks in the CP_FP8_KV role.  Scales must be
+ * powers of two from 2^-126 to 2^127 (only their exponents are read; they
+ * live in device memory and are not checked).  The ring moves the one-byte
+ * codes (half the bytes of bf16).  Both products run on the FP8 matrix cores with float32
  * accumulation; P is rounded to e4m3 for the P V product and l sums the same
  * rounded values.  out is bf16 (desc->dtype must be CP_BF16); m, l, lse as in
  * cp_attn_rank_forward; workspace of cp_attn_workspace_bytes(desc).

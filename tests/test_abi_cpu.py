@@ -412,18 +412,30 @@ def test_quantize_fp8_argument_errors():
     lib = B.lib()
     d = _desc()
     S1 = 0x1000
+    KV, QR = B.CP_FP8_KV, B.CP_FP8_QUERY
     cases = [
-        ((_desc(dtype="f32").ref, FAKE, FAKE, FAKE, S1), B.CP_ERR_UNSUPPORTED, "bf16"),
-        ((d.ref, None, FAKE, FAKE, S1), B.CP_ERR_INVALID_ARG, "x is NULL"),
-        ((d.ref, FAKE, None, FAKE, S1), B.CP_ERR_INVALID_ARG, "codes is NULL"),
-        ((d.ref, FAKE, FAKE + 4, FAKE, S1), B.CP_ERR_INVALID_ARG, "8-byte"),
-        ((d.ref, FAKE, FAKE, None, S1), B.CP_ERR_INVALID_ARG, "scales is NULL"),
-        ((d.ref, FAKE, FAKE, FAKE + 2, S1), B.CP_ERR_INVALID_ARG, "scales is not 4-byte"),
+        ((_desc(dtype="f32").ref, FAKE, KV, FAKE, FAKE, S1), B.CP_ERR_UNSUPPORTED, "bf16"),
+        ((d.ref, FAKE, 2, FAKE, FAKE, S1), B.CP_ERR_INVALID_ARG, "unknown FP8 role 2"),
+        ((d.ref, FAKE, -1, FAKE, FAKE, S1), B.CP_ERR_INVALID_ARG, "unknown FP8 role -1"),
+        ((d.ref, None, QR, FAKE, FAKE, S1), B.CP_ERR_INVALID_ARG, "x is NULL"),
+        ((d.ref, FAKE, KV, None, FAKE, S1), B.CP_ERR_INVALID_ARG, "codes is NULL"),
+        ((d.ref, FAKE, QR, FAKE + 4, FAKE, S1), B.CP_ERR_INVALID_ARG, "8-byte"),
+        ((d.ref, FAKE, KV, FAKE, None, S1), B.CP_ERR_INVALID_ARG, "scales is NULL"),
+        ((d.ref, FAKE, QR, FAKE, FAKE + 2, S1), B.CP_ERR_INVALID_ARG, "scales is not 4-byte"),
     ]
     for args, status, msg in cases:
         st = _status(lib.cp_attn_quantize_fp8, *args)
         assert st == status, (msg, st, B.last_error())
         assert msg in B.last_error(), (msg, B.last_error())
+
+
+def test_header_constants_match_binding():
+    """The #define'd flags and roles of include/cpattn.h have the binding's values."""
+    import re
+    text = open(HEADER).read()
+    defs = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (CP_[A-Z0-9_]+) (-?\d+)\b", text)}
+    for name in ("CP_RING_PREFETCH", "CP_RING_REVERSE", "CP_MAX_RING", "CP_FP8_KV", "CP_FP8_QUERY"):
+        assert defs[name] == getattr(B, name), name
 
 
 def test_rank_forward_fp8_argument_errors():

@@ -1,20 +1,31 @@
 """GPU parity of the FP8 (e4m3) path against the oracle (oracle/fp8.py).
 
 Quantisation is byte work, so its bar is bit-exact: every code and every
-float32 scale equals the oracle's, on ragged lengths (L not a multiple of
-the 256 rows a workgroup covers), both head dims, heads of very different
+float32 (power-of-two) scale equals the oracle's, in both roles (keys and
+values; the query, multiplied by the softmax scale times log2(e) first, for
+the default and a given softmax scale), on ragged lengths (L not a multiple
+of the 256 rows a workgroup covers), both head dims, heads of very different
 magnitudes, an all-zero head, and a full-size 128K block (all scales, codes
 of sampled rows).
 
 The FP8 shard forward is compared with the oracle's float64 attention on the
-dequantised inputs (the oracle quantises the same bf16 draws itself).  Its
-tolerance follows from the arithmetic of the kernel:
+dequantised inputs (the oracle quantises the same bf16 draws itself, the
+query with its base-2 factor).  The kernel takes P = exp2(x - m_ref) two
+ways: exp2 of the logit with the conversion dividing by 2^m_ref, or, when a
+reference leaves the range where that is exact, exp2 of x - m_ref; logits
+hundreds of units above or below zero drive the second way
+(test_fp8_forward_logit_range).  The tolerance follows from the arithmetic of
+the kernel:
   * scores: products of two e4m3 values are exact in float32 and are summed
-    over at most 128 head dims in float32, so m (the row max) differs from the
-    oracle's only by float32 rounding, at most 128 * 2^-24 = 2^-17 of the sum
-    of the products' magnitudes, which stays below 8 |m| for the row max on
-    these inputs: max-abs 2e-3 + 2^-14 |m| (the bf16 path's 2e-3, plus the
-    term that matters for heads whose scores reach hundreds);
+    over at most 128 head dims in float32 (the power-of-two scales are
+    exact), so each score, and with it m (the row max), differs from the
+    oracle's by float32 rounding of at most 128 * 2^-24 = 2^-17 of the sum of
+    the products' magnitudes.  That sum is bounded per row, for every key the
+    row sees, by A = scale * sum_d |q_d| max_k |k_d| (the maximum over all
+    keys of the supplied blocks, from the dequantised inputs); it can exceed
+    |m| many times over (a row of one visible key whose score is near zero).
+    Bound: max-abs 2e-3 + 2^-17 A + 2^-20 |m| (the bf16 path's 2e-3; the last
+    term covers log2(e) and ln(2) rounded to float32);
   * P = exp(s - m_ref) is rounded to e4m3 before the P V product and l sums
     the same rounded values.  A normal e4m3 value is within 2^-4 (half of the
     3-bit mantissa's ulp) of its argument, relative; over a log-uniform
@@ -55,27 +66,30 @@ def cp():
     return cp
 
 
-def _quantize_gpu(cp, x, d):
+def _quantize_gpu(cp, x, d, role=None, scale=0.0):
     B, L, H, _ = x.shape
-    desc = cp.Desc(B, H, d, 1, L, 0, "bf16", "none")
+    desc = cp.Desc(B, H, d, 1, L, 0, "bf16", "none", scale=scale)
     codes = torch.empty((B, L, H, d), dtype=torch.uint8, device="cuda")
     scales = torch.full((B, H), float("nan"), device="cuda")
-    cp.cp_attn_quantize_fp8(desc, dev(x, "bf16"), codes, scales)
+    cp.cp_attn_quantize_fp8(desc, dev(x, "bf16"), codes, scales, role=cp.CP_FP8_KV if role is None else role)
     torch.cuda.synchronize()
     return codes.cpu().numpy(), scales.cpu().numpy()
 
 
+@pytest.mark.parametrize("role", ["kv", "query", "query_scale"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("L", [1, 300, 513])
-def test_quantize_bit_exact(cp, d, L):
+def test_quantize_bit_exact(cp, d, L, role):
     rng = np.random.default_rng(L + d)
     x = rng.standard_normal((2, L, 4, d)).astype(np.float32) * np.array([1.0, 1e-3, 50.0, 1.0], np.float32)[None, None, :, None]
     x[1, :, 3, :] = 0.0                                   # one all-zero (b, h)
     x[0, 0, 0, :4] = [0.0, -0.0, 1e-30, -1e-30]           # zeros and values far below the smallest code
     x = round_to_bf16(x)
-    say(f"[fp8 quantize] L={L} d={d}")
-    codes, scales = _quantize_gpu(cp, x, d)
-    ref = F.quantize_heads(x)
+    say(f"[fp8 quantize] L={L} d={d} role={role}")
+    sm = 0.3 if role == "query_scale" else 0.0
+    c = 1.0 if role == "kv" else F.query_prescale(d, sm)
+    codes, scales = _quantize_gpu(cp, x, d, cp.CP_FP8_KV if role == "kv" else cp.CP_FP8_QUERY, sm)
+    ref = F.quantize_heads(x, c)
     assert np.array_equal(scales.view(np.uint32), ref["scale"].view(np.uint32)), "scales differ"
     bad = np.argwhere(codes != ref["codes"])
     assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[0].tolist()}: gpu {codes[tuple(bad[0])]:#x} " \
@@ -83,24 +97,42 @@ def test_quantize_bit_exact(cp, d, L):
 
 
 def test_quantize_full_size_block(cp):
-    """One K block of the 128K example (L = 32768, H = 32, d = 128)."""
+    """One K block of the 128K example (L = 32768, H = 32, d = 128) and the
+    same draws as a query: every scale, and the codes of sampled rows."""
     spec = ShardSpec(S=131072, N=4, H=32, d=128, dtype="bf16", mask="causal", cfg_id=3)
     x = draw_shard(spec, 0, TENSOR_K, 2)
-    codes, scales = _quantize_gpu(cp, x, 128)
-    amax = np.abs(x).max(axis=(1, 3))
-    ref_scale = (amax / np.float32(448)).astype(np.float32)
-    assert np.array_equal(scales.view(np.uint32), ref_scale.view(np.uint32)), "scales differ"
     rows = np.unique(np.concatenate([[0, 1, 255, 256, 32767], np.random.default_rng(5).integers(0, 32768, 64)]))
-    inv = (np.float32(448) / amax).astype(np.float32)
-    y = np.clip(x[:, rows] * inv[:, None, :, None], -448, 448).astype(np.float32)
-    ref_codes = F.e4m3_encode(y)
-    assert np.array_equal(codes[:, rows], ref_codes), "codes of sampled rows differ"
+    for role in (cp.CP_FP8_KV, cp.CP_FP8_QUERY):
+        say(f"[fp8 quantize full] role={role}")
+        c = np.float32(1.0) if role == cp.CP_FP8_KV else F.query_prescale(128)
+        codes, scales = _quantize_gpu(cp, x, 128, role)
+        # the oracle's steps on the whole block for the scales, on the sampled rows for the codes
+        amax = np.abs((x * c).astype(np.float32)).max(axis=(1, 3))
+        e = F.scale_exponent(amax)
+        assert np.array_equal(scales.view(np.uint32), np.exp2(e).astype(np.float32).view(np.uint32)), "scales differ"
+        ref = F.quantize_heads(x[:, rows], c)          # codes only: its scales are those of the sampled rows
+        y = (x[:, rows] * c).astype(np.float32).astype(np.float64) * np.exp2(-e.astype(np.float64))[:, None, :, None]
+        assert np.array_equal(codes[:, rows], F.e4m3_encode(np.clip(y, -448, 448))), "codes of sampled rows differ"
+        del ref
 
 
 # ----------------------------------------------------------------------------
 # the shard forward on e4m3 inputs
 
-FP8_TOL = dict(o_max=0.15, o_mean=1e-2, o_rel_rms=0.045, m_abs=2e-3, m_rel=2.0 ** -14, l_rel=0.07, lse_abs=0.07)
+FP8_TOL = dict(o_max=0.15, o_mean=1e-2, o_rel_rms=0.045, m_abs=2e-3, m_acc=2.0 ** -17, m_rel=2.0 ** -20, l_rel=0.07,
+               lse_abs=0.07)
+
+
+def _product_bound(spec, qz, kz, rows=None):
+    """A [B, H, rows] (natural-log units): scale * sum_d |q_d| max_k |k_d| over
+    the keys of the supplied blocks, a bound on the sum of the magnitudes of
+    one score's products, from the dequantised inputs."""
+    q = np.abs(F.dequantize_heads(qz["codes"], qz["scale"], F.query_prescale(spec.d)))     # [B, L, H, d]
+    if rows is not None:
+        q = q[:, rows]
+    kmax = np.max([np.abs(F.dequantize_heads(z["codes"], z["scale"])).max(axis=1) for z in kz if z is not None],
+                  axis=0)                                                                  # [B, H, d]
+    return np.einsum("blhd,bhd->bhl", q, kmax) / np.sqrt(spec.d)
 
 
 def _codes_dev(q):
@@ -129,7 +161,7 @@ def _run_fp8(cp, spec, rank, qc, qs, kc, ks, vc, vs, flags):
     return host(out), host(m), host(l), host(lse)
 
 
-def _check_fp8(got, ref, rows=None, heads=None):
+def _check_fp8(got, ref, A, rows=None, heads=None):
     o, m, l, lse = got
     if rows is not None:
         o = o[:, rows][:, :, heads]
@@ -147,7 +179,7 @@ def _check_fp8(got, ref, rows=None, heads=None):
     for name, g in (("m", m), ("l", l), ("lse", lse)):
         assert np.array_equal(np.isneginf(g), np.isneginf(ref[name])), f"{name}: -inf pattern differs"
     r_m = ref["m"][~ninf]
-    m_bound = t["m_abs"] + t["m_rel"] * np.abs(r_m)
+    m_bound = t["m_abs"] + t["m_acc"] * A[~ninf] + t["m_rel"] * np.abs(r_m)
     stats["m"] = float(np.max(np.abs(m[~ninf] - r_m) / m_bound, initial=0.0))     # fraction of the bound
     assert stats["m"] <= 1.0, f"m: {stats}"
     stats["l"] = float(np.max(np.abs(l[~ninf] / ref["l"][~ninf] - 1), initial=0.0))
@@ -159,7 +191,8 @@ def _check_fp8(got, ref, rows=None, heads=None):
 
 def _quantized_inputs(spec, seed, ranks):
     inp = make_inputs(spec, seed=seed, ranks=ranks)
-    qz = {r: F.quantize_heads(inp["q"][r]) for r in ranks}
+    c = F.query_prescale(spec.d)
+    qz = {r: F.quantize_heads(inp["q"][r], c) for r in ranks}
     kz = [F.quantize_heads(inp["k"][j]) for j in range(spec.N)]
     vz = [F.quantize_heads(inp["v"][j]) for j in range(spec.N)]
     return qz, kz, vz
@@ -168,7 +201,7 @@ def _quantized_inputs(spec, seed, ranks):
 def _oracle_fp8(spec, rank, qz, kz, vz, rows=None, heads=None):
     return F.fp8_rank_attention(qz["codes"], qz["scale"], [z["codes"] for z in kz], [z["scale"] for z in kz],
                                 [z["codes"] for z in vz], [z["scale"] for z in vz], rank, spec.N, spec.mask,
-                                spec.cu_seqlens, rows=rows, heads=heads)
+                                spec.cu_seqlens, rows=rows, heads=heads, q_prescale=F.query_prescale(spec.d))
 
 
 def _small_cu(S):
@@ -197,7 +230,7 @@ def test_fp8_forward_small_every_rank(cp, d, mask):
         qc, qs = _codes_dev(qz[r])
         got = _run_fp8(cp, spec, r, qc, qs, [x[0] for x in kd], [x[1] for x in kd], [x[0] for x in vd],
                        [x[1] for x in vd], cp.CP_RING_PREFETCH)
-        stats = _check_fp8(got, _oracle_fp8(spec, r, qz[r], kz, vz))
+        stats = _check_fp8(got, _oracle_fp8(spec, r, qz[r], kz, vz), _product_bound(spec, qz[r], kz))
         say(f"   {stats}")
 
 
@@ -214,7 +247,7 @@ def test_fp8_forward_ring_variants(cp, flags):
     say(f"[fp8 fwd ring] flags={flags}")
     got = _run_fp8(cp, spec, N - 1, qc, qs, [x[0] for x in kd], [x[1] for x in kd], [x[0] for x in vd],
                    [x[1] for x in vd], fl)
-    _check_fp8(got, _oracle_fp8(spec, N - 1, qz[N - 1], kz, vz))
+    _check_fp8(got, _oracle_fp8(spec, N - 1, qz[N - 1], kz, vz), _product_bound(spec, qz[N - 1], kz))
 
 
 @pytest.mark.parametrize("L", [1, 65])
@@ -232,7 +265,7 @@ def test_fp8_forward_degenerate(cp, L):
         inp["q"][r][:, :, 3, :] = 0.0
     for j in range(N):
         inp["k"][j] = round_to_bf16(inp["k"][j] * mag_k)
-    qz = {r: F.quantize_heads(inp["q"][r]) for r in range(N)}
+    qz = {r: F.quantize_heads(inp["q"][r], F.query_prescale(spec.d)) for r in range(N)}
     kz = [F.quantize_heads(inp["k"][j]) for j in range(N)]
     vz = [F.quantize_heads(inp["v"][j]) for j in range(N)]
     kd = [_codes_dev(z) for z in kz]
@@ -242,14 +275,58 @@ def test_fp8_forward_degenerate(cp, L):
         qc, qs = _codes_dev(qz[r])
         got = _run_fp8(cp, spec, r, qc, qs, [x[0] for x in kd], [x[1] for x in kd], [x[0] for x in vd],
                        [x[1] for x in vd], cp.CP_RING_PREFETCH)
-        _check_fp8(got, _oracle_fp8(spec, r, qz[r], kz, vz))
+        _check_fp8(got, _oracle_fp8(spec, r, qz[r], kz, vz), _product_bound(spec, qz[r], kz))
 
 
-def _quantize_dev(cp, x_dev, spec):
+def test_fp8_forward_logit_range(cp):
+    """Logits far outside the range where exp2(x) and 2^m_ref are normal
+    float32 values, so waves take the subtracting path: head 0 has all
+    scores near +400 (m_ref near +560 in base 2), head 1 near -400 (m_ref
+    near -560), head 2 has ordinary rows and, in the wave of rows 64-95,
+    rows 80 on 20 times larger, and the keys of the second block 20 times
+    larger from its row 100 on (global key 230): on rank 1 references leave
+    the range in the middle of a row, in a wave that mixes both kinds of
+    rows.  N = 2 shards of L = 130, causal, d = 64, every rank."""
+    N, L, H, d = 2, 130, 3, 64
+    spec = ShardSpec(S=N * L, N=N, H=H, d=d, dtype="bf16", mask="causal", cfg_id=114)
+    inp = make_inputs(spec, seed=6, ranks=range(N))
+    rng = np.random.default_rng(61)
+    for r in range(N):
+        q = inp["q"][r]
+        q[:, :, 0, :] = np.abs(rng.standard_normal((1, L, d))) * 4 + 4
+        q[:, :, 1, :] = np.abs(rng.standard_normal((1, L, d))) * 4 + 4
+        q[:, 80:, 2, :] *= 20
+        inp["q"][r] = round_to_bf16(q)
+    for j in range(N):
+        k = inp["k"][j]
+        k[:, :, 0, :] = np.abs(rng.standard_normal((1, L, d))) * 4 + 4
+        k[:, :, 1, :] = -(np.abs(rng.standard_normal((1, L, d))) * 4 + 4)
+        if j == 1:
+            k[:, 100:, 2, :] *= 20                 # global keys 230 on
+        inp["k"][j] = round_to_bf16(k)
+    c = F.query_prescale(d)
+    qz = {r: F.quantize_heads(inp["q"][r], c) for r in range(N)}
+    kz = [F.quantize_heads(inp["k"][j]) for j in range(N)]
+    vz = [F.quantize_heads(inp["v"][j]) for j in range(N)]
+    kd = [_codes_dev(z) for z in kz]
+    vd = [_codes_dev(z) for z in vz]
+    for r in range(N):
+        ref = _oracle_fp8(spec, r, qz[r], kz, vz)
+        m2 = ref["m"] / np.log(2.0)
+        say(f"[fp8 fwd logit range] rank={r}: base-2 row max per head "
+            f"{[(float(np.min(m2[0, h])), float(np.max(m2[0, h]))) for h in range(H)]}")
+        assert np.min(m2[0, 0]) > 130 and np.max(m2[0, 1]) < -130, "the heads do not reach the subtracting path"
+        qc, qs = _codes_dev(qz[r])
+        got = _run_fp8(cp, spec, r, qc, qs, [x[0] for x in kd], [x[1] for x in kd], [x[0] for x in vd],
+                       [x[1] for x in vd], cp.CP_RING_PREFETCH)
+        say(f"   {_check_fp8(got, ref, _product_bound(spec, qz[r], kz))}")
+
+
+def _quantize_dev(cp, x_dev, spec, role):
     desc = cp.Desc(spec.B, spec.H, spec.d, 1, spec.L, 0, "bf16", "none")
     codes = torch.empty(x_dev.shape, dtype=torch.uint8, device="cuda")
     scales = torch.empty((spec.B, spec.H), device="cuda")
-    cp.cp_attn_quantize_fp8(desc, x_dev, codes, scales)
+    cp.cp_attn_quantize_fp8(desc, x_dev, codes, scales, role=role)
     return codes, scales
 
 
@@ -264,8 +341,9 @@ def test_fp8_forward_full_size(cp, cfg):
     heads = sorted({0, spec.H - 1, int(np.random.default_rng(cfg + 17).integers(spec.H))})
     say(f"[fp8 full cfg {cfg}] {spec.name}: blocks {blocks}, heads {heads}")
     q = draw_shard(spec, 0, TENSOR_Q, spec.rank)
-    qc, qs = _quantize_dev(cp, dev(q, "bf16"), spec)
-    qz = F.quantize_heads(q[:, :, heads])
+    c = F.query_prescale(spec.d)
+    qc, qs = _quantize_dev(cp, dev(q, "bf16"), spec, cp.CP_FP8_QUERY)
+    qz = F.quantize_heads(q[:, :, heads], c)
     assert np.array_equal(qc.cpu().numpy()[:, :, heads], qz["codes"])
     del q
     kc, ks, vc, vs = ([None] * spec.N for _ in range(4))
@@ -273,7 +351,7 @@ def test_fp8_forward_full_size(cp, cfg):
     for j in blocks:
         for tid, cs_, ss_, zz in ((TENSOR_K, kc, ks, kz), (TENSOR_V, vc, vs, vz)):
             x = draw_shard(spec, 0, tid, j)
-            cs_[j], ss_[j] = _quantize_dev(cp, dev(x, "bf16"), spec)
+            cs_[j], ss_[j] = _quantize_dev(cp, dev(x, "bf16"), spec, cp.CP_FP8_KV)
             zz[j] = F.quantize_heads(x[:, :, heads])
             del x
             assert np.array_equal(cs_[j].cpu().numpy()[:, :, heads], zz[j]["codes"]), f"codes of block {j}"
@@ -286,8 +364,8 @@ def test_fp8_forward_full_size(cp, cfg):
     ref = F.fp8_rank_attention(qz["codes"], qz["scale"], [z["codes"] if z else None for z in kz],
                                [z["scale"] if z else None for z in kz], [z["codes"] if z else None for z in vz],
                                [z["scale"] if z else None for z in vz], spec.rank, spec.N, spec.mask,
-                               spec.cu_seqlens, rows=rows)
-    stats = _check_fp8(got, ref, rows=rows, heads=heads)
+                               spec.cu_seqlens, rows=rows, q_prescale=c)
+    stats = _check_fp8(got, ref, _product_bound(spec, qz, kz, rows=rows), rows=rows, heads=heads)
     say(f"[fp8 full cfg {cfg}] {len(rows)} rows x {len(heads)} heads: {stats}")
     for arr in got:
         assert np.all(np.isfinite(arr))

@@ -122,11 +122,11 @@ def _fp8_fwd(cp):
     return f
 
 
-def _quantize(cp, x):
+def _quantize(cp, x, role):
     desc = cp.Desc(1, H, D, 1, L, 0, "bf16", "none")
     codes = torch.empty((1, L, H, D), dtype=torch.uint8, device="cuda")
     scales = torch.empty((1, H), device="cuda")
-    cp.cp_attn_quantize_fp8(desc, x, codes, scales)
+    cp.cp_attn_quantize_fp8(desc, x, codes, scales, role=role)
     return codes, scales
 
 
@@ -155,9 +155,9 @@ def test_ring_order_bf16(cp, N, mask):
 def test_ring_order_fp8(cp, N, mask):
     spec = _spec(N, mask)
     q, k, v = _inputs(spec)
-    qc, qs = _quantize(cp, q)
-    kq = [_quantize(cp, t) for t in k]
-    vq = [_quantize(cp, t) for t in v]
+    qc, qs = _quantize(cp, q, cp.CP_FP8_QUERY)
+    kq = [_quantize(cp, t, cp.CP_FP8_KV) for t in k]
+    vq = [_quantize(cp, t, cp.CP_FP8_KV) for t in v]
     torch.cuda.synchronize()
     _check_variants(cp, spec, _fp8_fwd(cp), qc, [c for c, _ in kq], [c for c, _ in vq],
                     (qs, [s for _, s in kq], [s for _, s in vq]), "fp8")
