@@ -123,16 +123,18 @@ FP8_TOL = dict(o_max=0.15, o_mean=1e-2, o_rel_rms=0.045, m_abs=2e-3, m_acc=2.0 *
                lse_abs=0.07)
 
 
-def _product_bound(spec, qz, kz, rows=None):
+def _product_bound(spec, qz, kz, rows=None, scale=None):
     """A [B, H, rows] (natural-log units): scale * sum_d |q_d| max_k |k_d| over
     the keys of the supplied blocks, a bound on the sum of the magnitudes of
-    one score's products, from the dequantised inputs."""
-    q = np.abs(F.dequantize_heads(qz["codes"], qz["scale"], F.query_prescale(spec.d)))     # [B, L, H, d]
+    one score's products, from the dequantised inputs (softmax scale
+    1/sqrt(d) unless given)."""
+    q = np.abs(F.dequantize_heads(qz["codes"], qz["scale"], F.query_prescale(spec.d, scale)))   # [B, L, H, d]
     if rows is not None:
         q = q[:, rows]
     kmax = np.max([np.abs(F.dequantize_heads(z["codes"], z["scale"])).max(axis=1) for z in kz if z is not None],
                   axis=0)                                                                  # [B, H, d]
-    return np.einsum("blhd,bhd->bhl", q, kmax) / np.sqrt(spec.d)
+    sm = scale if scale else 1.0 / np.sqrt(spec.d)
+    return np.einsum("blhd,bhd->bhl", q, kmax) * sm
 
 
 def _codes_dev(q):
@@ -276,6 +278,45 @@ def test_fp8_forward_degenerate(cp, L):
         got = _run_fp8(cp, spec, r, qc, qs, [x[0] for x in kd], [x[1] for x in kd], [x[0] for x in vd],
                        [x[1] for x in vd], cp.CP_RING_PREFETCH)
         _check_fp8(got, _oracle_fp8(spec, r, qz[r], kz, vz), _product_bound(spec, qz[r], kz))
+
+
+def test_fp8_forward_given_scale(cp):
+    """A softmax scale given in the desc (0.3 instead of 1/sqrt(d)): the query
+    is quantised under that desc, with the scale folded into its codes, and
+    the forward under the same desc matches the oracle's attention with that
+    scale.  N = 2 shards of L = 200, causal, d = 64, H = 2, both ranks."""
+    N, L, H, d, sm = 2, 200, 2, 64, 0.3
+    spec = ShardSpec(S=N * L, N=N, H=H, d=d, dtype="bf16", mask="causal", cfg_id=115)
+    inp = make_inputs(spec, seed=8, ranks=range(N))
+    kz = [F.quantize_heads(inp["k"][j]) for j in range(N)]
+    vz = [F.quantize_heads(inp["v"][j]) for j in range(N)]
+    kd = [_codes_dev(z) for z in kz]
+    vd = [_codes_dev(z) for z in vz]
+    for r in range(N):
+        say(f"[fp8 fwd given scale] rank={r}")
+        desc_q = cp.Desc(1, H, d, 1, L, 0, "bf16", "none", scale=sm)
+        qc = torch.empty((1, L, H, d), dtype=torch.uint8, device="cuda")
+        qs = torch.empty((1, H), device="cuda")
+        cp.cp_attn_quantize_fp8(desc_q, dev(inp["q"][r], "bf16"), qc, qs, role=cp.CP_FP8_QUERY)
+        c = F.query_prescale(d, sm)
+        qz = F.quantize_heads(inp["q"][r], c)
+        assert np.array_equal(qc.cpu().numpy(), qz["codes"]), "query codes differ from the oracle's"
+        desc = cp.Desc(1, H, d, N, L, r, "bf16", "causal", scale=sm)
+        out = torch.full((1, L, H, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        m, l, lse = (torch.full((1, H, L), float("nan"), device="cuda") for _ in range(3))
+        ws = cp.alloc_workspace(desc)
+        cs, xs = torch.cuda.Stream(), torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            cp.cp_attn_rank_forward_fp8(desc, qc, qs, [x[0] for x in kd], [x[1] for x in kd], [x[0] for x in vd],
+                                        [x[1] for x in vd], out, m, l, lse, workspace=ws, compute_stream=cs,
+                                        copy_stream=xs, flags=cp.CP_RING_PREFETCH)
+        torch.cuda.synchronize()
+        ref = F.fp8_rank_attention(qz["codes"], qz["scale"], [z["codes"] for z in kz], [z["scale"] for z in kz],
+                                   [z["codes"] for z in vz], [z["scale"] for z in vz], r, N, "causal", scale=sm,
+                                   q_prescale=c)
+        A = _product_bound(spec, qz, kz, scale=sm)
+        say(f"   {_check_fp8((host(out), host(m), host(l), host(lse)), ref, A)}")
 
 
 def test_fp8_forward_logit_range(cp):
