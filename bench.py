@@ -308,6 +308,39 @@ def _timed_flushed(fn, stream, warmup: int, reps: int, flush) -> dict:
     return {"median": float(np.median(t)), "mean": float(np.mean(t))}
 
 
+def _timed_rotating(fn, stream, warmup: int, reps: int) -> dict:
+    """Per-iteration HIP-event times of fn(i) on `stream`, back to back, where
+    fn(i) works on input set i mod (number of sets): with the sets together
+    more than twice the 256 MB Infinity Cache, each iteration reads inputs
+    that earlier iterations have evicted, as a ring step reads a freshly
+    received block, and no other kernel runs between iterations.  Returns
+    the median, mean, min and max in ms."""
+    import torch
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = []
+    for i in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn(i)
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return {"median": float(np.median(t)), "mean": float(np.mean(t)), "min": t[0], "max": t[-1]}
+
+
+# Cold-input sets: enough copies of a workload's inputs to span twice the
+# 256 MB Infinity Cache.
+MALL_BYTES = 256 << 20
+
+
+def _n_sets(set_bytes: int) -> int:
+    return max(2, -(-2 * MALL_BYTES // set_bytes) + 1)
+
+
 SECONDARY = ("cfg2", "cfg5", "cfg4", "ulysses", "fp8")
 # Untimed calls before timing a workload of about a millisecond: its first few
 # dozen calls run up to 10 % slower than the steady state (the kernels' own
@@ -321,9 +354,11 @@ def secondary(seed: int, reps: int = 5, only=None):
     the bidirectional 64K merge stress case (8 PARTIAL_LSE launches, then one
     merge in a shuffled order; the merge is reported against HBM), one rank's
     share of all-to-all (Ulysses) context parallelism at 128K and the FP8
-    forward.  The 32K shard and the merge stress case fit in the caches, so
-    they are timed per iteration with the caches flushed in between (median of
-    10).  `only` names one of SECONDARY to run alone (for a profiler run)."""
+    forward.  The inputs of the 32K shard would stay in the caches, so it and
+    the merge stress case are timed over rotating copies of their inputs,
+    each evicted before reuse (medians), with the medians of calls each after
+    a cache-flushing read reported beside them.  `only` names one of
+    SECONDARY to run alone (for a profiler run)."""
     import torch
 
     import context_ring_attention_cp_amd as cp
@@ -356,8 +391,11 @@ def _dev_bf16(x):
 
 def _sec_ring(cp, spec, seed, cs, xs, reps):
     """A rank forward with ring prefetch: the causal 32K last-rank shard (its
-    K/V would stay in the caches, so each iteration follows a 512 MiB cache
-    flush; median of 10) or the packed-document shard (mean of reps)."""
+    inputs would stay in the caches, so it is timed over rotating copies of
+    its inputs that are evicted before reuse: median of 40 back-to-back
+    calls; the median of 10 calls each after a 512 MiB cache-flushing read is
+    reported beside it) or the packed-document shard (mean of reps; its
+    inputs exceed the caches)."""
     import torch
 
     from harness.inputs import TENSOR_K, TENSOR_Q, TENSOR_V, draw_shard
@@ -371,16 +409,30 @@ def _sec_ring(cp, spec, seed, cs, xs, reps):
     o = torch.empty((1, spec.L, spec.H, spec.d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((1, spec.H, spec.L), device="cuda")
     ws = cp.alloc_workspace(desc)
-    run = lambda: cp.cp_attn_rank_forward(desc, q, kb, vb, o, None, None, lse, workspace=ws,  # noqa: E731
-                                          compute_stream=cs, copy_stream=xs, flags=cp.CP_RING_PREFETCH)
+    sets = [(q, kb, vb)]
+
+    def run(i=0):
+        qq, kk, vv = sets[i % len(sets)]
+        cp.cp_attn_rank_forward(desc, qq, kk, vv, o, None, None, lse, workspace=ws, compute_stream=cs,
+                                copy_stream=xs, flags=cp.CP_RING_PREFETCH)
+
     fl = attn_flops(spec, cp.cp_attn_visible_pairs(desc))
     extra = {}
     if spec.S <= 32768:
-        flush = torch.ones(128 << 20, device="cuda")     # 512 MiB
-        t = _timed_flushed(run, cs, SHORT_WARMUP, 10, flush)
+        set_bytes = sum(t.numel() * t.element_size() for t in [q] + [t for t in kb + vb if t is not None])
+        for _ in range(_n_sets(set_bytes) - 1):
+            sets.append((q.clone(), [None if t is None else t.clone() for t in kb],
+                         [None if t is None else t.clone() for t in vb]))
+        t = _timed_rotating(run, cs, SHORT_WARMUP, 40)
         ms = t["median"]
-        extra = {"ms_mean": round(t["mean"], 4), "timing": "median of 10, caches flushed between iterations"}
+        flush = torch.ones(128 << 20, device="cuda")     # 512 MiB
+        tf = _timed_flushed(run, cs, SHORT_WARMUP, 10, flush)
         del flush
+        extra = {"ms_mean": round(t["mean"], 4), "ms_min_max": [round(t["min"], 4), round(t["max"], 4)],
+                 "timing": f"median of 40 back-to-back calls over {len(sets)} rotating copies of the inputs "
+                           f"({len(sets)} x {set_bytes / 2**20:.0f} MiB, each evicted from the caches before reuse)",
+                 "ms_flushed": round(tf["median"], 4),
+                 "tflops_flushed": round(fl / (tf["median"] * 1e-3) / 1e12, 2)}
     else:
         ms = _timed(run, cs, SHORT_WARMUP, reps)
     # per-launch attention kernel times of one more call
@@ -389,6 +441,7 @@ def _sec_ring(cp, spec, seed, cs, xs, reps):
                             copy_stream=xs, flags=cp.CP_RING_PREFETCH, profiler=prof)
     kms = prof.read()
     prof.close()
+    del sets
     return {"workload": spec.name, "blocks": sched, "ms": round(ms, 4),
             "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
             "pct_of_peak": round(100.0 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
@@ -397,8 +450,11 @@ def _sec_ring(cp, spec, seed, cs, xs, reps):
 
 def _sec_merge(cp, spec, seed, cs):
     """Bidirectional 64K over 8 ranks, rank 5, Q x 3: eight PARTIAL_LSE
-    launches, then one merge in a seeded shuffled order (caches flushed by a
-    512 MiB read before each iteration; median of 10)."""
+    launches, then one merge in a seeded shuffled order.  Timed over two
+    rotating copies of the inputs and of the partials (each set larger than
+    the 256 MB Infinity Cache): partials median of 10, merge median of 40; the
+    medians with a 512 MiB cache-flushing read before each call are reported
+    beside them."""
     import torch
 
     from harness.inputs import TENSOR_K, TENSOR_Q, TENSOR_V, draw_shard, shuffled_order
@@ -407,36 +463,48 @@ def _sec_merge(cp, spec, seed, cs):
     kb = [_dev_bf16(draw_shard(spec, seed, TENSOR_K, j)) for j in range(spec.N)]
     vb = [_dev_bf16(draw_shard(spec, seed, TENSOR_V, j)) for j in range(spec.N)]
     big, vec = (1, spec.L, spec.H, spec.d), (1, spec.H, spec.L)
-    op = [torch.empty(big, device="cuda") for _ in range(spec.N)]
-    lp = [torch.empty(vec, device="cuda") for _ in range(spec.N)]
+    ins = [(q, kb, vb), (q.clone(), [t.clone() for t in kb], [t.clone() for t in vb])]
+    parts = [([torch.empty(big, device="cuda") for _ in range(spec.N)],
+              [torch.empty(vec, device="cuda") for _ in range(spec.N)]) for _ in range(2)]
     o = torch.empty(big, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(vec, device="cuda")
     order = shuffled_order(seed, 4, spec.N)
-    flush = torch.ones(128 << 20, device="cuda")
 
-    def partials():
+    def partials(i=0):
+        qq, kk, vv = ins[i % 2]
+        op, lp = parts[i % 2]
         with torch.cuda.stream(cs):
             for j in range(spec.N):
-                cp.cp_attn_block_partial(desc, j, cp.CP_MODE_PARTIAL_LSE, q, kb[j], vb[j], o_part=op[j],
+                cp.cp_attn_block_partial(desc, j, cp.CP_MODE_PARTIAL_LSE, qq, kk[j], vv[j], o_part=op[j],
                                          lse_part=lp[j], stream=cs)
 
-    def merge():
+    def merge(i=0):
+        op, lp = parts[i % 2]
         cp.cp_attn_merge_lse(desc, op, lp, order, o, lse, stream=cs)
 
-    # the partials' inputs (9 x 32 MiB) and the merge's (8 x 64 MiB partials) would stay in the caches
-    tp = _timed_flushed(partials, cs, 2, 10, flush)
-    tm = _timed_flushed(merge, cs, SHORT_WARMUP, 10, flush)
+    tp = _timed_rotating(partials, cs, 2, 10)
+    tm = _timed_rotating(merge, cs, SHORT_WARMUP, 40)
+    flush = torch.ones(128 << 20, device="cuda")
+    tpf = _timed_flushed(partials, cs, 1, 10, flush)
+    tmf = _timed_flushed(merge, cs, SHORT_WARMUP, 10, flush)
+    del flush
     ms_p, ms_m = tp["median"], tm["median"]
     fl = attn_flops(spec, cp.cp_attn_visible_pairs(desc))
     rows = spec.L * spec.H
     merge_bytes = spec.N * rows * (spec.d * 4 + 4) + rows * (spec.d * 2 + 4)
-    return {"workload": spec.name, "order": order, "timing": "median of 10, caches flushed between iterations",
-            "partials_ms_mean": round(tp["mean"], 4), "merge_ms_mean": round(tm["mean"], 4),
-            "partials_ms": round(ms_p, 4),
-            "partials_tflops": round(fl / (ms_p * 1e-3) / 1e12, 2), "merge_ms": round(ms_m, 4),
-            "merge_algorithmic_bytes": merge_bytes,
-            "merge_gbs": round(merge_bytes / (ms_m * 1e-3) / 1e9, 1),
-            "merge_frac_of_hbm": round(merge_bytes / (ms_m * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    gbs = lambda ms: merge_bytes / (ms * 1e-3) / 1e9      # noqa: E731
+    res = {"workload": spec.name, "order": order,
+           "timing": "medians over two rotating copies of the inputs and partials (partials 10 calls, merge 40)",
+           "partials_ms_mean": round(tp["mean"], 4), "merge_ms_mean": round(tm["mean"], 4),
+           "partials_ms": round(ms_p, 4),
+           "partials_tflops": round(fl / (ms_p * 1e-3) / 1e12, 2), "merge_ms": round(ms_m, 4),
+           "merge_algorithmic_bytes": merge_bytes,
+           "merge_gbs": round(gbs(ms_m), 1),
+           "merge_frac_of_hbm": round(gbs(ms_m) / PEAK_HBM_GBS, 4),
+           "partials_ms_flushed": round(tpf["median"], 4), "merge_ms_flushed": round(tmf["median"], 4),
+           "merge_gbs_flushed": round(gbs(tmf["median"]), 1)}
+    del ins, parts
+    return res
 
 
 def _sec_ulysses(cp, spec, seed, cs, reps):
