@@ -51,8 +51,8 @@
 //   core as well: one more MFMA per tile with an all-ones A operand
 //   (1.0 = code 0x38) and a P^T operand leaves sum_k P[q][k] in every
 //   accumulator element of query q's lanes.  That MFMA falls in the compute
-//   phase, which is shorter than the softmax phase here, and saves the softmax
-//   the decode and the adds of 32 values per lane per tile.
+//   phase and saves the softmax the decode and the adds of 32 values per lane
+//   per tile.
 // Tiles are 128 keys x d bytes (16 KiB at d = 128), 4 stages, 128 KiB of LDS:
 //   with FP8 products a 64-key tile is too little work per phase to carry the
 //   phase's fixed costs (barriers, waits, the row max exchange); 128-key tiles
