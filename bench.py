@@ -435,17 +435,30 @@ def _sec_ring(cp, spec, seed, cs, xs, reps):
                  "tflops_flushed": round(fl / (tf["median"] * 1e-3) / 1e12, 2)}
     else:
         ms = _timed(run, cs, SHORT_WARMUP, reps)
-    # per-launch attention kernel times of one more call
-    prof = cp.Profiler(len(sched))
-    cp.cp_attn_rank_forward(desc, q, kb, vb, o, None, None, lse, workspace=ws, compute_stream=cs,
-                            copy_stream=xs, flags=cp.CP_RING_PREFETCH, profiler=prof)
-    kms = prof.read()
-    prof.close()
+    # per-launch attention kernel and receive times: medians of 10 profiled
+    # calls with the receives beside the kernels (prefetch) and after them on
+    # the compute stream (serial), which shows what the overlap costs the
+    # kernels that share the compute units with the copies
+    def per_launch(flags):
+        ks, rs = [], []
+        for _ in range(10):
+            prof = cp.Profiler(len(sched))
+            cp.cp_attn_rank_forward(desc, q, kb, vb, o, None, None, lse, workspace=ws, compute_stream=cs,
+                                    copy_stream=xs, flags=flags, profiler=prof)
+            ks.append(prof.read())
+            rs.append(prof.read_copies())
+            prof.close()
+        med = lambda col: round(float(np.median(col)), 4)
+        return ([med([k[i] for k in ks]) for i in range(len(ks[0]))],
+                [med([r[i] for r in rs]) for i in range(len(rs[0]))])
+    kms, rms = per_launch(cp.CP_RING_PREFETCH)
+    kms_serial, rms_serial = per_launch(0)
     del sets
     return {"workload": spec.name, "blocks": sched, "ms": round(ms, 4),
             "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
             "pct_of_peak": round(100.0 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-            "kernel_ms": [round(x, 4) for x in kms], **extra}
+            "kernel_ms": kms, "receive_ms": rms,
+            "kernel_ms_serial": kms_serial, "receive_ms_serial": rms_serial, **extra}
 
 
 def _sec_merge(cp, spec, seed, cs):
