@@ -348,7 +348,7 @@ SECONDARY = ("cfg2", "cfg5", "cfg4", "ulysses", "fp8")
 SHORT_WARMUP = 30
 
 
-def secondary(seed: int, reps: int = 5, only=None):
+def secondary(seed: int, reps: int = 5, only=None, streams=None):
     """The other workloads of the path, timed briefly: the causal 32K
     last-rank shard, the packed-document shard (rank_forward, ring prefetch),
     the bidirectional 64K merge stress case (8 PARTIAL_LSE launches, then one
@@ -358,7 +358,11 @@ def secondary(seed: int, reps: int = 5, only=None):
     the merge stress case are timed over rotating copies of their inputs,
     each evicted before reuse (medians), with the medians of calls each after
     a cache-flushing read reported beside them.  `only` names one of
-    SECONDARY to run alone (for a profiler run)."""
+    SECONDARY to run alone (for a profiler run).  `streams`: the (compute,
+    copy) stream pair to use; a process keeps its streams on few hardware
+    queues, and two more streams beside the headline's can land the copy
+    stream on the compute stream's queue, which serialises the receives with
+    the kernels they should overlap."""
     import torch
 
     import context_ring_attention_cp_amd as cp
@@ -366,7 +370,7 @@ def secondary(seed: int, reps: int = 5, only=None):
 
     out = {}
     cfgs = standard_configs(seed)
-    cs, xs = torch.cuda.Stream(), torch.cuda.Stream()
+    cs, xs = streams if streams is not None else (torch.cuda.Stream(), torch.cuda.Stream())
     for name in SECONDARY:
         if only is not None and name != only:
             continue
@@ -771,7 +775,7 @@ def main():
     del qd, kd, vd, out, lse
     if not args.no_secondary:
         log("[bench] secondary workloads")
-        res["secondary"] = secondary(args.seed)
+        res["secondary"] = secondary(args.seed, streams=(cs, xs))
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows of head 0")
         res["cpu_baseline"] = cpu_baseline(spec, q, k, v, args.cpu_rows)
